@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for the FLARE++ mixer forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check in
+__graft_entry__ and by the CPU-baseline leg of bench.py, never by the GPU
+library or its Python binding.
+"""
+from .flarepp_oracle import *  # noqa: F401,F403
+from .flarepp_oracle import __all__  # noqa: F401
