@@ -1,0 +1,186 @@
+/*
+ * libflarepp: forward pass of the FLARE++ token mixer (and two-step FLARE)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed, for every batch element b and head h, with s = 1/sqrt(D):
+ *
+ *   sigma = 1 / (1 + exp(-g_h))                                   (gate)
+ *   q_dyn = softmax_rows(s q0_h k0_bh^T) k0_bh                    (synthesis)
+ *   q     = q_fixed_h + sigma q_dyn                               (routing query)
+ *   z     = softmax_rows(s q k_bh^T) v_bh                         (encode, N -> M)
+ *   y_bh  = softmax_rows(s k_bh q^T) z                            (decode, M -> N)
+ *
+ * Sources: "FLARE++ and FLARE: Low-rank attention routing for PDE
+ * surrogates" (FLARE.py README), section "FLARE++" (core mixer listing: three
+ * scaled-dot-product attention calls with the default 1/sqrt(D) scale, k0 as
+ * both synthesis key and value) and section "FLARE" (two-step mixer); issue
+ * "[FEA]: Update FLARE++ to the v2 reference design and add token-sharded
+ * context parallelism for FLARE/FLARE++ #2024", section "Changes from v1 to
+ * v2" (q = q_fixed + sigma(g) q_dynamic; gate closed gives FLARE; shared
+ * synthesis keys and values) and section "Multi-GPU context parallelism"
+ * (exact split encoder with log-sum-exp statistics, used here across
+ * token chunks of one GPU).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Tensor pointers are DEVICE pointers to contiguous row-major arrays.
+ *   Token tensors are [B, H, N, D]; latent tensors [H, M, D] are shared by
+ *   all batch elements.  Element type is given by `dtype` (flarepp_dtype);
+ *   the gate is always fp32.
+ * - Arithmetic: products accumulate in fp32; softmax statistics are fp32;
+ *   intermediates q, z are kept in fp32 and rounded to the input dtype only
+ *   where they feed a matrix-core product.  The output is rounded to the
+ *   input dtype (round to nearest even).  fp32 inputs use an fp32 path with
+ *   no reduced-precision step.
+ * - Ownership: the caller owns every buffer (inputs, output, workspace).
+ *   The library allocates nothing per call and keeps no pointer after the
+ *   call returns.
+ * - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *   default stream) and nothing is synchronised; results are valid once the
+ *   caller synchronises that stream, and inputs must stay alive until then.
+ *   One workspace must not be used by two calls in flight on different
+ *   streams at the same time.
+ * - Errors: the return value is a flarepp_status.  All argument checks run
+ *   before any launch; on error nothing is enqueued.  Errors raised inside
+ *   kernels surface at the caller's next synchronisation.  Non-finite values
+ *   in the token or latent tensors propagate (NaN in, NaN out); the gate
+ *   may be +/-inf.
+ * - Results are deterministic: the token chunking depends only on the
+ *   shape, and no atomics are used.
+ */
+#ifndef FLAREPP_H
+#define FLAREPP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLAREPP_F32 = 0,
+  FLAREPP_BF16 = 1,
+  FLAREPP_F16 = 2
+} flarepp_dtype;
+
+typedef enum {
+  FLAREPP_OK = 0,
+  FLAREPP_ERR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, overflow, bad dtype,
+                                       non-finite or non-positive scale, output
+                                       aliasing an input */
+  FLAREPP_ERR_UNSUPPORTED = 2,      /* D not in {8,16,32,64}, M > 512, or the
+                                       current device is not gfx950 */
+  FLAREPP_ERR_WORKSPACE = 3,        /* workspace NULL, too small or not 256-byte
+                                       aligned */
+  FLAREPP_ERR_HIP = 4               /* a HIP runtime call or launch failed, or no
+                                       device is present */
+} flarepp_status;
+
+/* Largest number of latents M the kernels accept (the decode keeps the
+ * routing queries and the encoded latents of one head resident in LDS). */
+#define FLAREPP_MAX_M 512
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* flarepp_status_string(int status);
+
+/* Library version as "major.minor.patch" (static storage). */
+const char* flarepp_version(void);
+
+/*
+ * Workspace bytes needed by flarepp_mixer_fwd / flare_mixer_fwd for this
+ * shape and dtype.  Returns 0 if the arguments are invalid or unsupported
+ * (same checks as the compute calls, minus pointers and device).
+ * The workspace holds the per-chunk softmax partials of the split encoder
+ * and the operand copies of q and z; it needs 256-byte alignment.
+ */
+size_t flarepp_workspace_size(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                              int dtype);
+
+/*
+ * FLARE++ mixer forward: y = mixer(q0, q_fixed, gate, k0, k, v), scale
+ * 1/sqrt(D) in all three attention steps ("FLARE++" listing, FLARE.py
+ * README; gate from issue #2024 "Fixed reference and gate").
+ *
+ *   q0, q_fixed : [H, M, D] dtype   learned seeds and fixed routing queries
+ *   gate        : [H] fp32          gate LOGITS g; sigma(g) is applied inside.
+ *                                   g = -inf closes the gate: the synthesis
+ *                                   step is skipped on the device for that head
+ *                                   and the head computes FLARE exactly.
+ *   k0          : [B, H, N, D]      synthesis keys, also the synthesis values
+ *   k, v        : [B, H, N, D]      keys and values of the input tokens
+ *   y           : [B, H, N, D]      output, written; must not overlap any input
+ *   workspace   : >= flarepp_workspace_size(B,H,N,M,D,dtype) bytes, 256-aligned
+ *   stream      : hipStream_t (NULL = default stream)
+ */
+int flarepp_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                      const void* q0, const void* q_fixed, const float* gate,
+                      const void* k0, const void* k, const void* v, void* y,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Two-step FLARE mixer forward (FLARE.py README, section "FLARE"):
+ *   z = softmax_rows(scale q k^T) v ;  y = softmax_rows(scale k q^T) z.
+ * The listing on that page uses scale = 1.0; a closed-gate FLARE++ head
+ * equals this call with scale = 1/sqrt(D).
+ *
+ *   q     : [H, M, D] dtype  latent queries
+ *   k, v  : [B, H, N, D]     keys and values
+ *   y     : [B, H, N, D]     output, written; must not overlap any input
+ *   scale : finite and > 0
+ *   workspace as for flarepp_mixer_fwd (the same size function applies).
+ */
+int flare_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                    float scale, const void* q, const void* k, const void* v, void* y,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes for flare_encode_fwd with a given token chunk length
+ * (chunk_tokens = 0 selects the same chunking as the mixer calls).
+ */
+size_t flare_encode_workspace_size(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                   int dtype, int64_t chunk_tokens);
+
+/*
+ * Encoder alone (the "flare_encode" step named in issue #2024, "Multi-GPU
+ * context parallelism"): z = softmax_rows(scale q k^T) v, computed as
+ * per-chunk partials (row max, row sum, unnormalised output) over token
+ * chunks of `chunk_tokens` tokens and merged with log-sum-exp weights.
+ *
+ *   q              : [H, M, D] dtype if q_batch_stride == 0, else [B, H, M, D]
+ *                    with q_batch_stride == H*M*D elements
+ *   k, v           : [B, H, N, D] dtype (v may equal k)
+ *   z              : [B, H, M, D] fp32, written
+ *   chunk_tokens   : 0 = default chunking; otherwise a positive multiple of 64
+ *   workspace      : >= flare_encode_workspace_size(..., chunk_tokens)
+ */
+int flare_encode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                     float scale, const void* q, int64_t q_batch_stride,
+                     const void* k, const void* v, float* z, int64_t chunk_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for flare_decode_fwd. */
+size_t flare_decode_workspace_size(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                   int dtype);
+
+/*
+ * Decoder alone: y = softmax_rows(scale k q^T) z, the softmax running over
+ * the M latents of each token (third call of the FLARE++ listing, second
+ * call of the FLARE listing).
+ *
+ *   q  : [H, M, D] dtype if q_batch_stride == 0, else [B, H, M, D] with
+ *        q_batch_stride == H*M*D
+ *   z  : [B, H, M, D] fp32 latent values
+ *   k  : [B, H, N, D] dtype token keys (the queries of this step)
+ *   y  : [B, H, N, D] dtype, written; must not overlap any input
+ */
+int flare_decode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                     float scale, const void* q, int64_t q_batch_stride, const float* z,
+                     const void* k, void* y, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLAREPP_H */

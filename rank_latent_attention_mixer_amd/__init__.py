@@ -1,0 +1,272 @@
+"""Python binding of libflarepp (FLARE++ token-mixer forward on MI355X).
+
+Argument marshalling only: tensors are passed to the C ABI as raw device
+pointers together with torch's current HIP stream; every step of the
+computation runs in the library's HIP kernels.  torch supplies device memory
+(outputs and workspace) and the stream.  There is no fallback: if the
+library is missing, loading it raises.
+
+Entry points (same names as the C ABI in include/flarepp.h):
+
+* ``flarepp_mixer_fwd(q0, q_fixed, gate, k0, k, v)`` -> y
+* ``flare_mixer_fwd(q, k, v, scale)`` -> y
+* ``flare_encode_fwd(q, k, v, scale, chunk_tokens=0)`` -> z (fp32)
+* ``flare_decode_fwd(q, z, k, scale)`` -> y
+* ``flarepp_workspace_size(B, H, N, M, D, dtype)`` and friends
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+__all__ = [
+    "FlareppError", "load_library", "library_path", "dtype_code",
+    "flarepp_mixer_fwd", "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
+    "flarepp_workspace_size", "flare_encode_workspace_size", "flare_decode_workspace_size",
+    "flarepp_status_string", "flarepp_version", "declared_functions",
+    "FLAREPP_OK", "FLAREPP_ERR_INVALID_ARGUMENT", "FLAREPP_ERR_UNSUPPORTED",
+    "FLAREPP_ERR_WORKSPACE", "FLAREPP_ERR_HIP", "FLAREPP_F32", "FLAREPP_BF16", "FLAREPP_F16",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "flarepp.h")
+
+FLAREPP_OK = 0
+FLAREPP_ERR_INVALID_ARGUMENT = 1
+FLAREPP_ERR_UNSUPPORTED = 2
+FLAREPP_ERR_WORKSPACE = 3
+FLAREPP_ERR_HIP = 4
+FLAREPP_F32, FLAREPP_BF16, FLAREPP_F16 = 0, 1, 2
+
+_lib = None
+
+
+class FlareppError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {flarepp_status_string(status)} ({status})")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libflarepp.so")
+
+
+def load_library():
+    """Load libflarepp.so (built in-tree by build_lib.py); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m rank_latent_attention_mixer_amd.build_lib`"
+            " (there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    i64, sz, vp, i32, f32 = (ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                             ctypes.c_float)
+    shape = [i64] * 5
+    lib.flarepp_status_string.argtypes = [i32]
+    lib.flarepp_status_string.restype = ctypes.c_char_p
+    lib.flarepp_version.argtypes = []
+    lib.flarepp_version.restype = ctypes.c_char_p
+    lib.flarepp_workspace_size.argtypes = shape + [i32]
+    lib.flarepp_workspace_size.restype = sz
+    lib.flare_encode_workspace_size.argtypes = shape + [i32, i64]
+    lib.flare_encode_workspace_size.restype = sz
+    lib.flare_decode_workspace_size.argtypes = shape + [i32]
+    lib.flare_decode_workspace_size.restype = sz
+    lib.flarepp_mixer_fwd.argtypes = shape + [i32] + [vp] * 7 + [vp, sz, vp]
+    lib.flarepp_mixer_fwd.restype = i32
+    lib.flare_mixer_fwd.argtypes = shape + [i32, f32] + [vp] * 4 + [vp, sz, vp]
+    lib.flare_mixer_fwd.restype = i32
+    lib.flare_encode_fwd.argtypes = shape + [i32, f32, vp, i64, vp, vp, vp, i64, vp, sz, vp]
+    lib.flare_encode_fwd.restype = i32
+    lib.flare_decode_fwd.argtypes = shape + [i32, f32, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.flare_decode_fwd.restype = i32
+    _lib = lib
+    return lib
+
+
+def declared_functions():
+    """Function names declared in include/flarepp.h."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flare\w*)\s*\(", text)))
+
+
+def flarepp_status_string(status: int) -> str:
+    return load_library().flarepp_status_string(int(status)).decode()
+
+
+def flarepp_version() -> str:
+    return load_library().flarepp_version().decode()
+
+
+def flarepp_workspace_size(B, H, N, M, D, dtype) -> int:
+    return int(load_library().flarepp_workspace_size(B, H, N, M, D, dtype))
+
+
+def flare_encode_workspace_size(B, H, N, M, D, dtype, chunk_tokens=0) -> int:
+    return int(load_library().flare_encode_workspace_size(B, H, N, M, D, dtype, chunk_tokens))
+
+
+def flare_decode_workspace_size(B, H, N, M, D, dtype) -> int:
+    return int(load_library().flare_decode_workspace_size(B, H, N, M, D, dtype))
+
+
+# --------------------------------------------------------------------------
+# torch marshalling
+# --------------------------------------------------------------------------
+
+def dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FLAREPP_F32, torch.bfloat16: FLAREPP_BF16, torch.float16: FLAREPP_F16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes, device, workspace):
+    import torch
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _call(fn, where, *args):
+    st = fn(*args)
+    if st != FLAREPP_OK:
+        raise FlareppError(st, where)
+
+
+def flarepp_mixer_fwd(q0, q_fixed, gate, k0, k, v, y=None, workspace=None, stream=None):
+    """FLARE++ mixer forward; see include/flarepp.h.  Returns y."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q0.shape[1]
+    dev, dt = k.device, k.dtype
+    for name, t, shp in (("q0", q0, (H, M, D)), ("q_fixed", q_fixed, (H, M, D)),
+                         ("k0", k0, (B, H, N, D)), ("k", k, (B, H, N, D)),
+                         ("v", v, (B, H, N, D))):
+        _check_tensor(name, t, shp, dt, dev)
+    _check_tensor("gate", gate, (H,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, H, N, D), dtype=dt, device=dev)
+    _check_tensor("y", y, (B, H, N, D), dt, dev)
+    code = dtype_code(k)
+    nbytes = lib.flarepp_workspace_size(B, H, N, M, D, code)
+    if nbytes == 0:
+        raise FlareppError(FLAREPP_ERR_UNSUPPORTED, "flarepp_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    _call(lib.flarepp_mixer_fwd, "flarepp_mixer_fwd", B, H, N, M, D, code, _ptr(q0),
+          _ptr(q_fixed), _ptr(gate), _ptr(k0), _ptr(k), _ptr(v), _ptr(y), _ptr(ws),
+          ws.numel(), _stream(stream))
+    return y
+
+
+def flare_mixer_fwd(q, k, v, scale, y=None, workspace=None, stream=None):
+    """Two-step FLARE forward with an explicit scale.  Returns y."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q.shape[1]
+    dev, dt = k.device, k.dtype
+    for name, t, shp in (("q", q, (H, M, D)), ("k", k, (B, H, N, D)), ("v", v, (B, H, N, D))):
+        _check_tensor(name, t, shp, dt, dev)
+    if y is None:
+        y = torch.empty((B, H, N, D), dtype=dt, device=dev)
+    _check_tensor("y", y, (B, H, N, D), dt, dev)
+    code = dtype_code(k)
+    nbytes = lib.flarepp_workspace_size(B, H, N, M, D, code)
+    if nbytes == 0:
+        raise FlareppError(FLAREPP_ERR_UNSUPPORTED, "flarepp_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    _call(lib.flare_mixer_fwd, "flare_mixer_fwd", B, H, N, M, D, code, float(scale), _ptr(q),
+          _ptr(k), _ptr(v), _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
+    return y
+
+
+def flare_encode_fwd(q, k, v, scale, chunk_tokens=0, z=None, workspace=None, stream=None):
+    """Encoder alone: z = softmax(scale q k^T) v in fp32.  q is [H,M,D] (shared
+    over the batch) or [B,H,M,D]."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q.shape[-2]
+    dev, dt = k.device, k.dtype
+    qshape = (H, M, D) if q.dim() == 3 else (B, H, M, D)
+    _check_tensor("q", q, qshape, dt, dev)
+    _check_tensor("k", k, (B, H, N, D), dt, dev)
+    _check_tensor("v", v, (B, H, N, D), dt, dev)
+    if z is None:
+        z = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    _check_tensor("z", z, (B, H, M, D), torch.float32, dev)
+    code = dtype_code(k)
+    nbytes = lib.flare_encode_workspace_size(B, H, N, M, D, code, chunk_tokens)
+    if nbytes == 0:
+        raise FlareppError(FLAREPP_ERR_INVALID_ARGUMENT, "flare_encode_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    qbs = 0 if q.dim() == 3 else H * M * D
+    _call(lib.flare_encode_fwd, "flare_encode_fwd", B, H, N, M, D, code, float(scale), _ptr(q),
+          qbs, _ptr(k), _ptr(v), _ptr(z), int(chunk_tokens), _ptr(ws), ws.numel(),
+          _stream(stream))
+    return z
+
+
+def flare_decode_fwd(q, z, k, scale, y=None, workspace=None, stream=None):
+    """Decoder alone: y = softmax over latents of (scale k q^T), applied to z."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q.shape[-2]
+    dev, dt = k.device, k.dtype
+    qshape = (H, M, D) if q.dim() == 3 else (B, H, M, D)
+    _check_tensor("q", q, qshape, dt, dev)
+    _check_tensor("z", z, (B, H, M, D), torch.float32, dev)
+    _check_tensor("k", k, (B, H, N, D), dt, dev)
+    if y is None:
+        y = torch.empty((B, H, N, D), dtype=dt, device=dev)
+    _check_tensor("y", y, (B, H, N, D), dt, dev)
+    code = dtype_code(k)
+    nbytes = lib.flare_decode_workspace_size(B, H, N, M, D, code)
+    if nbytes == 0:
+        raise FlareppError(FLAREPP_ERR_UNSUPPORTED, "flare_decode_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    qbs = 0 if q.dim() == 3 else H * M * D
+    _call(lib.flare_decode_fwd, "flare_decode_fwd", B, H, N, M, D, code, float(scale), _ptr(q),
+          qbs, _ptr(z), _ptr(k), _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
+    return y
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

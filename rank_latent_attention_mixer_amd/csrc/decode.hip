@@ -1,0 +1,253 @@
+// Decoder y = softmax_rows(scale k q^T) z: every token attends over the M
+// latents (FLARE.py README, "FLARE++" listing, third attention call; "FLARE"
+// listing, scatter step).
+//
+// The latents of one (batch, head) -- routing queries q as keys and encoded
+// values z as values -- are loaded into LDS once per workgroup and stay
+// resident while the workgroup walks its token tiles (persistent over
+// tiles).  Tokens are the register side: each wave takes 64 tokens, loads
+// their k rows straight from HBM into matrix-core operands, sweeps the
+// latents 32 at a time with the shared online-softmax tile, and writes its
+// normalised y rows.  The value operand arrives with permuted rows so that
+// each lane holds 4*NDB contiguous output columns of one token.
+#include "flash_tile.hpp"
+#include "kernels.hpp"
+
+namespace flarepp {
+
+namespace {
+
+constexpr int kNC = 4;       // 16-token column blocks per wave
+constexpr int kNW = 8;       // waves per workgroup
+constexpr int kTokTile = 64 * kNW;
+
+template <int D>
+struct DecodeLds {
+  static constexpr int DV = D < 16 ? 16 : D;
+  static constexpr int KP = (D < 8 ? 8 : D) + 8;  // latent row pitch (elements)
+  static int zpitch(int Mk) { return Mk + 8; }
+  static int elems(int Mk) { return Mk * KP + DV * zpitch(Mk); }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kNW) void decode_kernel(DecodeParams a) {
+  using Tile = FlashTile<T, D, kNC>;
+  using V8 = typename Tile::V8;
+  constexpr int KD = Tile::KD, DV = Tile::DV, NDB = Tile::NDB;
+  constexpr int KP = DecodeLds<D>::KP;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  T* qs = reinterpret_cast<T*>(lds_raw);
+
+  const int Mk = (a.M + 31) & ~31;
+  const int ZP = Mk + 8;
+  T* zs = qs + Mk * KP;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int bh = blockIdx.x / a.wg_per_bh;
+  const int part = blockIdx.x - bh * a.wg_per_bh;
+  const int b = bh / a.H, h = bh - b * a.H;
+
+  // resident latents: q rows [0, Mk) and the value operand rows [0, DV)
+  {
+    const T* qg = reinterpret_cast<const T*>(a.q) + b * a.q_b_stride + h * a.q_h_stride;
+    constexpr int G8 = D / 8;
+    for (int u = tid; u < Mk * G8; u += 64 * kNW) {
+      const int row = u / G8, e = u - row * G8;
+      *reinterpret_cast<u32x4*>(&qs[row * KP + 8 * e]) = ldg16(qg + (int64_t)row * D + 8 * e);
+    }
+    const T* zg = reinterpret_cast<const T*>(a.zt) + (int64_t)bh * DV * a.Mpad;
+    const int zg8 = Mk / 8;
+    for (int u = tid; u < DV * zg8; u += 64 * kNW) {
+      const int row = u / zg8, e = u - row * zg8;
+      *reinterpret_cast<u32x4*>(&zs[row * ZP + 8 * e]) = ldg16(zg + (int64_t)row * a.Mpad + 8 * e);
+    }
+  }
+  __syncthreads();
+
+  const T* kg = reinterpret_cast<const T*>(a.k) + (int64_t)bh * a.N * D;
+  T* yg = reinterpret_cast<T*>(a.y) + (int64_t)bh * a.N * D;
+  const int64_t ntiles = (a.N + kTokTile - 1) / kTokTile;
+  const int nkt = Mk / 32;
+
+  for (int64_t tile = part; tile < ntiles; tile += a.wg_per_bh) {
+    const int64_t nb = tile * kTokTile + wave * 64;
+    if (nb >= a.N) continue;  // wave-uniform; no barrier below
+    Tile st;
+    st.reset();
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb) {
+      const int64_t n = nb + cb * 16 + r;
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) {
+        const int d0 = 32 * kd + 8 * g;
+        if (d0 < D && n < a.N) st.q[cb][kd] = bitcast_u4<V8>(ldg16(kg + n * D + d0));
+        else st.q[cb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+      }
+    }
+    for (int kt = 0; kt < nkt; ++kt) {
+      V8 kop[2][KD];
+      V8 vop[NDB];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd) {
+          const int d0 = 32 * kd + 8 * g;
+          if (d0 < D)
+            kop[jb][kd] = *reinterpret_cast<const V8*>(&qs[(32 * kt + 16 * jb + r) * KP + d0]);
+          else
+            kop[jb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        vop[db] = *reinterpret_cast<const V8*>(&zs[(16 * db + r) * ZP + 32 * kt + 8 * g]);
+      st.step(kop, vop, min(32, a.M - 32 * kt), g);
+    }
+    // y = O / l; lane (g, r) owns columns [g*4*NDB, (g+1)*4*NDB) of token r
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb) {
+      const float inv = 1.0f / st.row_sum(cb);
+      const int64_t n = nb + cb * 16 + r;
+      const int d0 = g * 4 * NDB;
+      if (n < a.N && d0 < D) {
+        T out[4 * NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[4 * db + i] = (T)(st.o[db][cb][i] * inv);
+        T* dst = yg + n * D + d0;
+        if constexpr (4 * NDB * sizeof(T) >= 16) {
+#pragma unroll
+          for (int w = 0; w < (int)(4 * NDB * sizeof(T)) / 16; ++w)
+            *reinterpret_cast<u32x4*>(dst + w * 8) = *reinterpret_cast<const u32x4*>(&out[w * 8]);
+        } else {
+          *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(&out[0]);
+        }
+      }
+    }
+  }
+}
+
+// fp32 path: one thread per token, latents streamed through LDS 32 at a time.
+template <int D>
+__global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams a) {
+  constexpr int TM = 32;
+  __shared__ float qsm[TM][D];
+  __shared__ float zsm[TM][D];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int64_t n = (int64_t)blockIdx.x * blockDim.x + tid;
+  const bool valid = n < a.N;
+  const float* kb = reinterpret_cast<const float*>(a.k) + (int64_t)bh * a.N * D;
+  const float* qb = reinterpret_cast<const float*>(a.q) + b * a.q_b_stride + h * a.q_h_stride;
+  const float* zb = reinterpret_cast<const float*>(a.zt) + (int64_t)bh * a.Mpad * D;
+  float kr[D], o[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    kr[d] = valid ? kb[n * D + d] : 0.f;
+    o[d] = 0.f;
+  }
+  float mref = -__builtin_inff(), l = 0.f;
+  for (int mb = 0; mb < a.M; mb += TM) {
+    const int tv = min(TM, a.M - mb);
+    for (int e = tid; e < TM * D; e += blockDim.x) {
+      const int j = e / D, d = e - j * D;
+      qsm[j][d] = j < tv ? qb[(int64_t)(mb + j) * D + d] : 0.f;
+      zsm[j][d] = j < tv ? zb[(int64_t)(mb + j) * D + d] : 0.f;
+    }
+    __syncthreads();
+    float s[TM];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc = fmaf(kr[d], qsm[j][d], acc);
+      s[j] = j < tv ? acc : -__builtin_inff();
+      mx = fmaxf(mx, s[j]);
+    }
+    if (mx > mref) {
+      const float sc = exp2f(mref - mx);
+      l *= sc;
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] *= sc;
+      mref = mx;
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const float p = exp2f(s[j] - mref);
+      l += p;
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] = fmaf(p, zsm[j][d], o[d]);
+    }
+    __syncthreads();
+  }
+  if (valid) {
+    float* yb = reinterpret_cast<float*>(a.y) + (int64_t)bh * a.N * D;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int d = 0; d < D; ++d) yb[n * D + d] = o[d] * inv;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
+  const int Mk = (p.M + 31) & ~31;
+  const size_t lds = (size_t)DecodeLds<D>::elems(Mk) * sizeof(T);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<T, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(p.B * p.H * p.wg_per_bh));
+  hipLaunchKernelGGL((decode_kernel<T, D>), grid, dim3(64 * kNW), lds, s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_mfma_d(int D, const DecodeParams& p, hipStream_t s) {
+  switch (D) {
+    case 8: return launch_mfma<T, 8>(p, s);
+    case 16: return launch_mfma<T, 16>(p, s);
+    case 32: return launch_mfma<T, 32>(p, s);
+    case 64: return launch_mfma<T, 64>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_f32(const DecodeParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)(p.B * p.H));
+  hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_lds_bytes(int M, int D, int dtype) {
+  if (dtype == kF32) return 0;
+  const int Mk = (M + 31) & ~31;
+  switch (D) {
+    case 8: return DecodeLds<8>::elems(Mk) * 2;
+    case 16: return DecodeLds<16>::elems(Mk) * 2;
+    case 32: return DecodeLds<32>::elems(Mk) * 2;
+    case 64: return DecodeLds<64>::elems(Mk) * 2;
+    default: return -1;
+  }
+}
+
+hipError_t launch_decode(int dtype, int D, const DecodeParams& p, hipStream_t s) {
+  if (dtype == kBF16) return launch_mfma_d<__bf16>(D, p, s);
+  if (dtype == kF16) return launch_mfma_d<_Float16>(D, p, s);
+  switch (D) {
+    case 8: return launch_f32<8>(p, s);
+    case 16: return launch_f32<16>(p, s);
+    case 32: return launch_f32<32>(p, s);
+    case 64: return launch_f32<64>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace flarepp

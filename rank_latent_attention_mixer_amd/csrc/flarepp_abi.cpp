@@ -1,0 +1,409 @@
+// C boundary of libflarepp: argument validation, workspace carving and the
+// launch sequence of each entry point.  See include/flarepp.h for the
+// contract (the operations are those of the FLARE.py README, "FLARE++" and
+// "FLARE" listings, with the gate of issue #2024 "Changes from v1 to v2").
+#include "../../include/flarepp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "kernels.hpp"
+
+namespace {
+
+using namespace flarepp;
+
+constexpr int kEncTile = 64;        // token tile of the encoder (chunk granularity)
+constexpr int kEncTargetWgs = 512;  // encoder workgroups aimed for (2 per CU)
+constexpr int kDecTokTile = 512;    // tokens per decoder workgroup iteration
+constexpr int kDecTargetWgs = 1024;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int esize_of(int dtype) { return dtype == FLAREPP_F32 ? 4 : 2; }
+
+struct Plan {
+  int64_t B, H, N, M, D;
+  int dtype;
+  int Mpad, DV;
+  int64_t chunk_tokens;
+  int nchunks;
+  int dec_wg_per_bh;
+  size_t off_pm, off_pl, off_po, off_q0, off_q, off_z, total;
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  return !__builtin_mul_overflow(a, b, out);
+}
+
+// Shape checks shared by every entry point (no HIP call).
+int check_shape(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype) {
+  if (B < 1 || H < 1 || N < 1 || M < 1 || D < 1) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (dtype != FLAREPP_F32 && dtype != FLAREPP_BF16 && dtype != FLAREPP_F16)
+    return FLAREPP_ERR_INVALID_ARGUMENT;
+  int64_t t;
+  if (!mul_ok(B, H, &t) || !mul_ok(t, N, &t) || !mul_ok(t, D, &t) || !mul_ok(t, 4, &t))
+    return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (!mul_ok(H, M, &t) || !mul_ok(t, D, &t)) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (B * H > (int64_t)1 << 24) return FLAREPP_ERR_INVALID_ARGUMENT;  // grid limits
+  if (D != 8 && D != 16 && D != 32 && D != 64) return FLAREPP_ERR_UNSUPPORTED;
+  if (M > FLAREPP_MAX_M) return FLAREPP_ERR_UNSUPPORTED;
+  return FLAREPP_OK;
+}
+
+int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+              int64_t chunk_tokens, Plan* p) {
+  int st = check_shape(B, H, N, M, D, dtype);
+  if (st != FLAREPP_OK) return st;
+  if (chunk_tokens < 0 || (chunk_tokens % kEncTile) != 0) return FLAREPP_ERR_INVALID_ARGUMENT;
+  p->B = B; p->H = H; p->N = N; p->M = M; p->D = D; p->dtype = dtype;
+  p->Mpad = latent_pad((int)M, dtype);
+  p->DV = D < 16 ? 16 : (int)D;
+  const int64_t BH = B * H;
+  const int64_t tiles = (N + kEncTile - 1) / kEncTile;
+  if (chunk_tokens == 0) {
+    int64_t c = (kEncTargetWgs + BH - 1) / BH;
+    if (c < 1) c = 1;
+    if (c > tiles) c = tiles;
+    const int64_t chunk_tiles = (tiles + c - 1) / c;
+    chunk_tokens = chunk_tiles * kEncTile;
+  }
+  const int64_t nchunks = (N + chunk_tokens - 1) / chunk_tokens;
+  int64_t wgs;
+  if (!mul_ok(BH, nchunks, &wgs) || wgs > 0x7FFFFFFF) return FLAREPP_ERR_INVALID_ARGUMENT;
+  p->chunk_tokens = chunk_tokens;
+  p->nchunks = (int)nchunks;
+  const int64_t dtiles = (N + kDecTokTile - 1) / kDecTokTile;
+  int64_t w = (kDecTargetWgs + BH - 1) / BH;
+  if (w > dtiles) w = dtiles;
+  if (w < 1) w = 1;
+  p->dec_wg_per_bh = (int)w;
+  if (!mul_ok(BH, w, &wgs) || wgs > 0x7FFFFFFF) return FLAREPP_ERR_INVALID_ARGUMENT;
+
+  const size_t es = (size_t)esize_of(dtype);
+  const size_t stat = (size_t)BH * nchunks * p->Mpad * sizeof(float);
+  size_t off = 0;
+  p->off_pm = off; off = align_up(off + stat);
+  p->off_pl = off; off = align_up(off + stat);
+  p->off_po = off; off = align_up(off + stat * D);
+  p->off_q0 = off; off = align_up(off + (size_t)H * p->Mpad * D * es);
+  p->off_q = off;  off = align_up(off + (size_t)BH * p->Mpad * D * es);
+  p->off_z = off;
+  off = align_up(off + (dtype == FLAREPP_F32 ? (size_t)BH * p->Mpad * D * 4
+                                             : (size_t)BH * p->DV * p->Mpad * es));
+  p->total = off;
+  return FLAREPP_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_workspace(const Plan& p, void* ws, size_t bytes) {
+  if (ws == nullptr || bytes < p.total || ((uintptr_t)ws % kAlign) != 0)
+    return FLAREPP_ERR_WORKSPACE;
+  return FLAREPP_OK;
+}
+
+// gfx950 check for the current device, cached per device id.
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLAREPP_ERR_HIP;
+  if (dev < 64) {
+    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return FLAREPP_OK;
+    if (c == 2) return FLAREPP_ERR_UNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FLAREPP_ERR_HIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FLAREPP_OK : FLAREPP_ERR_UNSUPPORTED;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FLAREPP_OK : FLAREPP_ERR_HIP; }
+
+unsigned char* ws_at(void* ws, size_t off) { return static_cast<unsigned char*>(ws) + off; }
+
+EncodeParams encode_params(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh,
+                           const void* k, const void* v, const float* gate) {
+  EncodeParams e;
+  e.q = q; e.q_b_stride = qb; e.q_h_stride = qh;
+  e.k = k; e.v = v;
+  e.B = (int)p.B; e.H = (int)p.H; e.N = p.N; e.M = (int)p.M; e.Mpad = p.Mpad;
+  e.chunk_tokens = p.chunk_tokens; e.nchunks = p.nchunks;
+  e.gate = gate;
+  e.part_m = reinterpret_cast<float*>(ws_at(ws, p.off_pm));
+  e.part_l = reinterpret_cast<float*>(ws_at(ws, p.off_pl));
+  e.part_o = reinterpret_cast<float*>(ws_at(ws, p.off_po));
+  return e;
+}
+
+CombineParams combine_base(const Plan& p, void* ws) {
+  CombineParams c;
+  std::memset(&c, 0, sizeof(c));
+  c.B = (int)p.B; c.H = (int)p.H; c.M = (int)p.M; c.Mpad = p.Mpad; c.D = (int)p.D; c.DV = p.DV;
+  c.part_m = reinterpret_cast<const float*>(ws_at(ws, p.off_pm));
+  c.part_l = reinterpret_cast<const float*>(ws_at(ws, p.off_pl));
+  c.part_o = reinterpret_cast<const float*>(ws_at(ws, p.off_po));
+  c.out_dtype = p.dtype;
+  return c;
+}
+
+// Operand copy of caller latents: out = scale*log2(e) * in, [sets][Mpad][D].
+hipError_t prep_latents(const Plan& p, void* ws, size_t off, const void* in, int64_t in_b_stride,
+                        int nsets, float cscale, hipStream_t s) {
+  CombineParams c = combine_base(p, ws);
+  c.nsets = nsets;
+  c.nchunks = 0;
+  c.mode = kModeQuery;
+  c.fixed = in;
+  c.fixed_b_stride = in_b_stride;
+  c.fixed_dtype = p.dtype;
+  c.force_fixed = 1;
+  c.cscale = cscale;
+  c.out = ws_at(ws, off);
+  c.out_kind = p.dtype == FLAREPP_F32 ? kOutNatural32 : kOutNatural;
+  return launch_combine(c, s);
+}
+
+hipError_t value_operand(const Plan& p, void* ws, int nchunks, const float* z_in, float* z_out,
+                         hipStream_t s) {
+  CombineParams c = combine_base(p, ws);
+  c.nsets = (int)(p.B * p.H);
+  c.nchunks = nchunks;
+  c.mode = kModeValue;
+  c.z_in = z_in;
+  c.z_out = z_out;
+  c.out = ws_at(ws, p.off_z);
+  c.out_kind = p.dtype == FLAREPP_F32 ? kOutNatural32 : kOutValueT;
+  return launch_combine(c, s);
+}
+
+hipError_t decode(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh, const void* k,
+                  void* y, hipStream_t s) {
+  DecodeParams d;
+  d.q = q; d.q_b_stride = qb; d.q_h_stride = qh;
+  d.zt = ws_at(ws, p.off_z);
+  d.k = k; d.y = y;
+  d.B = (int)p.B; d.H = (int)p.H; d.N = p.N; d.M = (int)p.M; d.Mpad = p.Mpad;
+  d.wg_per_bh = p.dec_wg_per_bh;
+  return launch_decode(p.dtype, (int)p.D, d, s);
+}
+
+#define FLAREPP_TRY(expr)                        \
+  do {                                           \
+    const hipError_t e_ = (expr);                \
+    if (e_ != hipSuccess) return FLAREPP_ERR_HIP; \
+  } while (0)
+
+int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, const void* q0,
+               const void* q_fixed, const float* gate, const void* k0, const void* k,
+               const void* v, void* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!q0 || !q_fixed || !gate || !k0 || !k || !v || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
+  Plan p;
+  int st = make_plan(B, H, N, M, D, dtype, 0, &p);
+  if (st != FLAREPP_OK) return st;
+  const size_t tok = (size_t)(B * H * N * D) * esize_of(dtype);
+  const size_t lat = (size_t)(H * M * D) * esize_of(dtype);
+  if (overlaps(y, tok, k0, tok) || overlaps(y, tok, k, tok) || overlaps(y, tok, v, tok) ||
+      overlaps(y, tok, q0, lat) || overlaps(y, tok, q_fixed, lat) ||
+      overlaps(y, tok, gate, (size_t)H * 4))
+    return FLAREPP_ERR_INVALID_ARGUMENT;
+  if ((st = check_workspace(p, ws, ws_bytes)) != FLAREPP_OK) return st;
+  if ((st = check_device()) != FLAREPP_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float c = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
+  const int64_t BH = B * H;
+  const int64_t qh = (int64_t)p.Mpad * D;
+  // 1. seeds as operand, 2. synthesis partials (closed-gate heads skipped)
+  FLAREPP_TRY(prep_latents(p, ws, p.off_q0, q0, 0, (int)H, c, s));
+  FLAREPP_TRY(launch_encode(dtype, (int)D,
+                            encode_params(p, ws, ws_at(ws, p.off_q0), 0, qh, k0, k0, gate), s));
+  // 3. q = q_fixed + sigma * q_dyn, per (b, h), as operand
+  {
+    CombineParams cp = combine_base(p, ws);
+    cp.nsets = (int)BH;
+    cp.nchunks = p.nchunks;
+    cp.mode = kModeQuery;
+    cp.fixed = q_fixed;
+    cp.fixed_b_stride = 0;
+    cp.fixed_dtype = dtype;
+    cp.gate = gate;
+    cp.cscale = c;
+    cp.out = ws_at(ws, p.off_q);
+    cp.out_kind = dtype == FLAREPP_F32 ? kOutNatural32 : kOutNatural;
+    FLAREPP_TRY(launch_combine(cp, s));
+  }
+  // 4. encode partials, 5. z as value operand, 6. decode
+  FLAREPP_TRY(launch_encode(dtype, (int)D,
+                            encode_params(p, ws, ws_at(ws, p.off_q), H * qh, qh, k, v, nullptr),
+                            s));
+  FLAREPP_TRY(value_operand(p, ws, p.nchunks, nullptr, nullptr, s));
+  FLAREPP_TRY(decode(p, ws, ws_at(ws, p.off_q), H * qh, qh, k, y, s));
+  (void)BH;
+  return FLAREPP_OK;
+}
+
+int flare_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, float scale,
+               const void* q, const void* k, const void* v, void* y, void* ws, size_t ws_bytes,
+               void* stream) {
+  if (!q || !k || !v || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
+  Plan p;
+  int st = make_plan(B, H, N, M, D, dtype, 0, &p);
+  if (st != FLAREPP_OK) return st;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FLAREPP_ERR_INVALID_ARGUMENT;
+  const size_t tok = (size_t)(B * H * N * D) * esize_of(dtype);
+  const size_t lat = (size_t)(H * M * D) * esize_of(dtype);
+  if (overlaps(y, tok, k, tok) || overlaps(y, tok, v, tok) || overlaps(y, tok, q, lat))
+    return FLAREPP_ERR_INVALID_ARGUMENT;
+  if ((st = check_workspace(p, ws, ws_bytes)) != FLAREPP_OK) return st;
+  if ((st = check_device()) != FLAREPP_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float c = (float)((double)scale * 1.4426950408889634);
+  const int64_t qh = (int64_t)p.Mpad * D;
+  FLAREPP_TRY(prep_latents(p, ws, p.off_q0, q, 0, (int)H, c, s));
+  FLAREPP_TRY(launch_encode(dtype, (int)D,
+                            encode_params(p, ws, ws_at(ws, p.off_q0), 0, qh, k, v, nullptr), s));
+  FLAREPP_TRY(value_operand(p, ws, p.nchunks, nullptr, nullptr, s));
+  FLAREPP_TRY(decode(p, ws, ws_at(ws, p.off_q0), 0, qh, k, y, s));
+  return FLAREPP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flarepp_status_string(int status) {
+  switch (status) {
+    case FLAREPP_OK: return "FLAREPP_OK";
+    case FLAREPP_ERR_INVALID_ARGUMENT: return "FLAREPP_ERR_INVALID_ARGUMENT";
+    case FLAREPP_ERR_UNSUPPORTED: return "FLAREPP_ERR_UNSUPPORTED";
+    case FLAREPP_ERR_WORKSPACE: return "FLAREPP_ERR_WORKSPACE";
+    case FLAREPP_ERR_HIP: return "FLAREPP_ERR_HIP";
+    default: return "FLAREPP_UNKNOWN_STATUS";
+  }
+}
+
+const char* flarepp_version(void) { return "0.1.0"; }
+
+size_t flarepp_workspace_size(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype) {
+  Plan p;
+  if (make_plan(B, H, N, M, D, dtype, 0, &p) != FLAREPP_OK) return 0;
+  return p.total;
+}
+
+size_t flare_encode_workspace_size(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                   int dtype, int64_t chunk_tokens) {
+  Plan p;
+  if (make_plan(B, H, N, M, D, dtype, chunk_tokens, &p) != FLAREPP_OK) return 0;
+  return p.total;
+}
+
+size_t flare_decode_workspace_size(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                   int dtype) {
+  return flarepp_workspace_size(B, H, N, M, D, dtype);
+}
+
+int flarepp_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                      const void* q0, const void* q_fixed, const float* gate, const void* k0,
+                      const void* k, const void* v, void* y, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  try {
+    return mixer_impl(B, H, N, M, D, dtype, q0, q_fixed, gate, k0, k, v, y, workspace,
+                      workspace_bytes, stream);
+  } catch (...) {
+    return FLAREPP_ERR_HIP;
+  }
+}
+
+int flare_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                    float scale, const void* q, const void* k, const void* v, void* y,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    return flare_impl(B, H, N, M, D, dtype, scale, q, k, v, y, workspace, workspace_bytes,
+                      stream);
+  } catch (...) {
+    return FLAREPP_ERR_HIP;
+  }
+}
+
+int flare_encode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                     float scale, const void* q, int64_t q_batch_stride, const void* k,
+                     const void* v, float* z, int64_t chunk_tokens, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  try {
+    if (!q || !k || !v || !z) return FLAREPP_ERR_INVALID_ARGUMENT;
+    Plan p;
+    int st = make_plan(B, H, N, M, D, dtype, chunk_tokens, &p);
+    if (st != FLAREPP_OK) return st;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FLAREPP_ERR_INVALID_ARGUMENT;
+    if (q_batch_stride != 0 && q_batch_stride != H * M * D) return FLAREPP_ERR_INVALID_ARGUMENT;
+    const size_t tok = (size_t)(B * H * N * D) * esize_of(dtype);
+    const size_t zb = (size_t)(B * H * M * D) * 4;
+    const size_t lat = (size_t)((q_batch_stride ? B : 1) * H * M * D) * esize_of(dtype);
+    if (overlaps(z, zb, k, tok) || overlaps(z, zb, v, tok) || overlaps(z, zb, q, lat))
+      return FLAREPP_ERR_INVALID_ARGUMENT;
+    if ((st = check_workspace(p, workspace, workspace_bytes)) != FLAREPP_OK) return st;
+    if ((st = check_device()) != FLAREPP_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float c = (float)((double)scale * 1.4426950408889634);
+    const int64_t qh = (int64_t)p.Mpad * D;
+    const bool per_batch = q_batch_stride != 0;
+    const size_t qoff = per_batch ? p.off_q : p.off_q0;
+    FLAREPP_TRY(prep_latents(p, workspace, qoff, q, q_batch_stride, (int)(per_batch ? B * H : H),
+                             c, s));
+    FLAREPP_TRY(launch_encode(dtype, (int)D,
+                              encode_params(p, workspace, ws_at(workspace, qoff),
+                                            per_batch ? H * qh : 0, qh, k, v, nullptr),
+                              s));
+    FLAREPP_TRY(value_operand(p, workspace, p.nchunks, nullptr, z, s));
+    return FLAREPP_OK;
+  } catch (...) {
+    return FLAREPP_ERR_HIP;
+  }
+}
+
+int flare_decode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                     float scale, const void* q, int64_t q_batch_stride, const float* z,
+                     const void* k, void* y, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  try {
+    if (!q || !z || !k || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
+    Plan p;
+    int st = make_plan(B, H, N, M, D, dtype, 0, &p);
+    if (st != FLAREPP_OK) return st;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FLAREPP_ERR_INVALID_ARGUMENT;
+    if (q_batch_stride != 0 && q_batch_stride != H * M * D) return FLAREPP_ERR_INVALID_ARGUMENT;
+    const size_t tok = (size_t)(B * H * N * D) * esize_of(dtype);
+    const size_t zb = (size_t)(B * H * M * D) * 4;
+    const size_t lat = (size_t)((q_batch_stride ? B : 1) * H * M * D) * esize_of(dtype);
+    if (overlaps(y, tok, k, tok) || overlaps(y, tok, z, zb) || overlaps(y, tok, q, lat))
+      return FLAREPP_ERR_INVALID_ARGUMENT;
+    if ((st = check_workspace(p, workspace, workspace_bytes)) != FLAREPP_OK) return st;
+    if ((st = check_device()) != FLAREPP_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float c = (float)((double)scale * 1.4426950408889634);
+    const int64_t qh = (int64_t)p.Mpad * D;
+    const bool per_batch = q_batch_stride != 0;
+    const size_t qoff = per_batch ? p.off_q : p.off_q0;
+    FLAREPP_TRY(prep_latents(p, workspace, qoff, q, q_batch_stride, (int)(per_batch ? B * H : H),
+                             c, s));
+    FLAREPP_TRY(value_operand(p, workspace, 0, z, nullptr, s));
+    FLAREPP_TRY(decode(p, workspace, ws_at(workspace, qoff), per_batch ? H * qh : 0, qh, k, y, s));
+    return FLAREPP_OK;
+  } catch (...) {
+    return FLAREPP_ERR_HIP;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device-side building blocks shared by the FLARE++ kernels (gfx950 only).
+//
+// Matrix-core tile used throughout: v_mfma_f32_16x16x32_{bf16,f16}.
+// For D[16x16] += A[16x32] * B[32x16], lane l of the 64-wide wave supplies
+//   A[l % 16][8*(l/16) .. 8*(l/16)+7]   (8 consecutive k of one row)
+//   B[8*(l/16) .. +7][l % 16]           (8 consecutive k of one column)
+// and receives D[4*(l/16) + i][l % 16], i = 0..3.
+//
+// Attention is evaluated "transposed": for query columns r (held in
+// registers) and keys j (streamed), the score tile is S^T[j][r] =
+// K[j] . Q[r], so each lane owns one query column and four keys.  Those four
+// fp32 scores of two 16-key blocks become, after exp and packing, exactly the
+// 8 k-values that lane must supply as the B operand of the P.V product
+// O^T[d][r] += V^T[d][j] P^T[j][r].  The price is that V must be supplied
+// transposed (rows d, k = keys) in the key order the score layout implies:
+// within a 32-key group, operand slot s = 8g + 4h + i holds key
+// j = 16h + 4g + i (g = lane group, h = which 16-key block, i = 0..3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flarepp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// log2(e): scores are carried in the base-2 domain so that exp is one
+// v_exp_f32.  The caller folds scale * log2(e) into the latent operand.
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Lazy rescaling threshold: probabilities of a tile may reach 2^kTau
+// relative to the running reference before the reference is moved.
+constexpr float kTauSum = 256.0f;  // 2^8
+
+template <typename T> struct Pack8;
+template <> struct Pack8<__bf16> { typedef bf16x8 type; typedef bf16x2 pair; };
+template <> struct Pack8<_Float16> { typedef f16x8 type; typedef f16x2 pair; };
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Sum of a packed pair plus an fp32 accumulator (v_dot2 with ones).
+__device__ __forceinline__ float pair_sum(bf16x2 p, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+}
+__device__ __forceinline__ float pair_sum(f16x2 p, float acc) {
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(p, ones, acc, false);
+}
+
+template <typename V>
+__device__ __forceinline__ V bitcast_u4(u32x4 x) {
+  return __builtin_bit_cast(V, x);
+}
+template <typename V>
+__device__ __forceinline__ u32x4 to_u4(V x) {
+  return __builtin_bit_cast(u32x4, x);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void stg16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Convert 8 fp32 to a packed 8-element operand (round to nearest even).
+template <typename T>
+__device__ __forceinline__ typename Pack8<T>::type pack8(float a0, float a1, float a2, float a3,
+                                                        float a4, float a5, float a6, float a7) {
+  typename Pack8<T>::type r;
+  r[0] = (T)a0; r[1] = (T)a1; r[2] = (T)a2; r[3] = (T)a3;
+  r[4] = (T)a4; r[5] = (T)a5; r[6] = (T)a6; r[7] = (T)a7;
+  return r;
+}
+
+// Operand slot of key j within a 32-key group (see header comment).
+__host__ __device__ __forceinline__ int key_slot(int j) {
+  const int h = j >> 4, g = (j >> 2) & 3, i = j & 3;
+  return 8 * g + 4 * h + i;
+}
+
+// Logistic gate in fp32; -inf -> 0, +inf -> 1.
+__device__ __forceinline__ float gate_sigma(float g) {
+  return 1.0f / (1.0f + expf(-g));
+}
+
+}  // namespace flarepp

@@ -1,0 +1,83 @@
+// Host-side launch interface of the FLARE++ kernels.  Everything here is
+// asynchronous on the given stream; shapes are validated by the caller
+// (flarepp_abi.cpp) before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flarepp {
+
+enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+// Split-N encoder partials (synthesis and encode steps).
+struct EncodeParams {
+  const void* q;          // latent operand [.., Mpad, D] (dtype, or fp32 on the fp32
+                          // path), prescaled by scale*log2(e); padded rows are zero
+  int64_t q_b_stride;     // elements between batch elements (0 = shared)
+  int64_t q_h_stride;     // elements between heads
+  const void* k;          // [B, H, N, D]
+  const void* v;          // [B, H, N, D]; may equal k
+  int B, H;
+  int64_t N;
+  int M, Mpad;
+  int64_t chunk_tokens;   // multiple of 64
+  int nchunks;
+  const float* gate;      // non-null: skip heads whose sigma(gate) == 0
+  float* part_m;          // [B*H, nchunks, Mpad] reference (base-2 units)
+  float* part_l;          // [B*H, nchunks, Mpad] sum of 2^(s - m)
+  float* part_o;          // [B*H, nchunks, Mpad, D] unnormalised outputs
+};
+
+// Merge of the partials plus the gated query update, or plain operand prep.
+struct CombineParams {
+  int B, H, M, Mpad, D, DV;
+  int nsets;              // latent sets written: B*H (per batch) or H (shared)
+  int nchunks;            // 0: no partials
+  const float* part_m;
+  const float* part_l;
+  const float* part_o;
+  int mode;               // kModeQuery or kModeValue
+  // query mode: q = fixed + sigma * merged (sigma = 0 -> q = fixed, partials unread)
+  const void* fixed;      // [.., H, M, D] in dtype `fixed_dtype`, or null
+  int64_t fixed_b_stride; // elements between batch elements of `fixed` (0 = shared)
+  int fixed_dtype;
+  const float* gate;      // gate logits [H]; null with force_fixed -> sigma = 0
+  int force_fixed;        // 1: ignore partials, q = fixed
+  float cscale;           // operand prescale scale*log2(e)
+  // value mode: z = merged, or z = z_in when nchunks == 0
+  const float* z_in;      // [B*H, M, D] fp32, or null
+  float* z_out;           // [B*H, M, D] fp32, or null
+  // operand written for the next step
+  void* out;
+  int out_kind;           // kOutNatural (dtype [sets][Mpad][D]), kOutValueT (dtype
+                          // [sets][DV][Mpad], slot order), kOutNatural32 (fp32 [sets][Mpad][D])
+  int out_dtype;
+};
+enum { kModeQuery = 0, kModeValue = 1 };
+enum { kOutNatural = 0, kOutValueT = 1, kOutNatural32 = 2 };
+
+// Decoder: y = softmax over latents of (k q^T) applied to z.
+struct DecodeParams {
+  const void* q;          // latent operand [.., Mpad, D] (prescaled)
+  int64_t q_b_stride, q_h_stride;
+  const void* zt;         // value operand: dtype [B*H][DV][Mpad] (slot order) or
+                          // fp32 [B*H][Mpad][D] on the fp32 path
+  const void* k;          // [B, H, N, D]
+  void* y;                // [B, H, N, D]
+  int B, H;
+  int64_t N;
+  int M, Mpad;
+  int wg_per_bh;
+};
+
+hipError_t launch_encode(int dtype, int D, const EncodeParams& p, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_decode(int dtype, int D, const DecodeParams& p, hipStream_t s);
+
+// Launch-shape helpers shared with the workspace sizing.
+int encode_waves(int M);                 // waves per encoder workgroup
+int latent_pad(int M, int dtype);        // Mpad
+int decode_lds_bytes(int M, int D, int dtype);
+
+}  // namespace flarepp

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/flarepp.h, sizes workspaces, and rejects every invalid
+argument before touching the device.  A valid call on a machine without a
+device returns FLAREPP_ERR_HIP instead of crashing.  No compute runs here."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import pytest
+
+import rank_latent_attention_mixer_amd as fp
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fp.library_path()),
+                                reason="libflarepp.so not built")
+
+OK, INV, UNS, WS, HIP = (fp.FLAREPP_OK, fp.FLAREPP_ERR_INVALID_ARGUMENT,
+                         fp.FLAREPP_ERR_UNSUPPORTED, fp.FLAREPP_ERR_WORKSPACE,
+                         fp.FLAREPP_ERR_HIP)
+
+# fake, distinct, 256-aligned addresses: never dereferenced because every
+# call below fails validation (or the device check) before any launch
+FAKE = {name: ctypes.c_void_p(0x10000000 * (i + 1)) for i, name in
+        enumerate(["q0", "qf", "gate", "k0", "k", "v", "y", "ws", "z"])}
+
+
+def lib():
+    return fp.load_library()
+
+
+def test_every_declared_function_is_exported():
+    names = fp.declared_functions()
+    assert {"flarepp_mixer_fwd", "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
+            "flarepp_workspace_size", "flarepp_status_string"} <= set(names)
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_status_strings_and_version():
+    for code, name in [(OK, "FLAREPP_OK"), (INV, "FLAREPP_ERR_INVALID_ARGUMENT"),
+                       (UNS, "FLAREPP_ERR_UNSUPPORTED"), (WS, "FLAREPP_ERR_WORKSPACE"),
+                       (HIP, "FLAREPP_ERR_HIP")]:
+        assert fp.flarepp_status_string(code) == name
+    assert fp.flarepp_status_string(99) == "FLAREPP_UNKNOWN_STATUS"
+    assert fp.flarepp_version().count(".") == 2
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+def test_workspace_sizes(dtype):
+    s = fp.flarepp_workspace_size(1, 8, 1 << 20, 512, 32, dtype)
+    assert s > 0 and s % 256 == 0
+    # grows with N only through the chunk count (partials are latent-sized)
+    assert fp.flarepp_workspace_size(1, 8, 1 << 21, 512, 32, dtype) == s
+    assert fp.flare_decode_workspace_size(1, 8, 1 << 20, 512, 32, dtype) == s
+    assert fp.flare_encode_workspace_size(1, 8, 1 << 20, 512, 32, dtype, 0) == s
+    # a finer chunking needs more partial storage
+    assert fp.flare_encode_workspace_size(1, 8, 1 << 20, 512, 32, dtype, 64) > s
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 8, 1024, 64, 32, 1), 0), ((1, 0, 1024, 64, 32, 1), 0), ((1, 8, 0, 64, 32, 1), 0),
+    ((1, 8, 1024, 0, 32, 1), 0), ((1, 8, 1024, 64, 0, 1), 0), ((1, 8, 1024, 64, 32, 3), 0),
+    ((1, 8, 1024, 64, 48, 1), 0), ((1, 8, 1024, 513, 32, 1), 0),
+    ((1 << 40, 1 << 20, 1 << 20, 64, 32, 1), 0),
+])
+def test_workspace_size_rejects(args, code):
+    assert fp.flarepp_workspace_size(*args) == code
+
+
+def test_encode_workspace_rejects_bad_chunk():
+    assert fp.flare_encode_workspace_size(1, 2, 1000, 16, 8, 0, 100) == 0
+    assert fp.flare_encode_workspace_size(1, 2, 1000, 16, 8, 0, -64) == 0
+    assert fp.flare_encode_workspace_size(1, 2, 1000, 16, 8, 0, 128) > 0
+
+
+def _mixer(B=1, H=2, N=1024, M=16, D=8, dt=1, q0="q0", qf="qf", gate="gate", k0="k0",
+           k="k", v="v", y="y", ws="ws", wsb=None):
+    ptr = lambda n: None if n is None else (n if isinstance(n, ctypes.c_void_p) else FAKE[n])
+    if wsb is None:
+        wsb = fp.flarepp_workspace_size(B, H, N, M, D, dt) or 1 << 30
+    return lib().flarepp_mixer_fwd(B, H, N, M, D, dt, ptr(q0), ptr(qf), ptr(gate), ptr(k0),
+                                   ptr(k), ptr(v), ptr(y), ptr(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q0=None), INV), (dict(qf=None), INV), (dict(gate=None), INV), (dict(k0=None), INV),
+    (dict(k=None), INV), (dict(v=None), INV), (dict(y=None), INV),
+    (dict(B=0), INV), (dict(H=-1), INV), (dict(N=0), INV), (dict(M=0), INV), (dict(D=0), INV),
+    (dict(dt=7), INV), (dict(D=12), UNS), (dict(D=128), UNS), (dict(M=600), UNS),
+    (dict(B=1 << 40, N=1 << 40), INV),
+    (dict(ws=None), WS), (dict(wsb=1), WS),
+    (dict(ws=ctypes.c_void_p(0x10000000 * 8 + 64)), WS),     # misaligned workspace
+    (dict(y="k"), INV), (dict(y="v"), INV), (dict(y="k0"), INV), (dict(y="q0"), INV),
+    (dict(y=ctypes.c_void_p(0x10000000 * 5 + 8)), INV),         # y overlaps k
+])
+def test_mixer_rejects_before_any_launch(kw, code):
+    assert _mixer(**kw) == code
+
+
+def test_valid_call_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert _mixer() == HIP
+
+
+def test_flare_rejects_bad_scale():
+    L = lib()
+    ws = fp.flarepp_workspace_size(1, 2, 64, 16, 8, 0)
+    for scale in (0.0, -1.0, float("inf"), float("nan")):
+        st = L.flare_mixer_fwd(1, 2, 64, 16, 8, 0, scale, FAKE["q0"], FAKE["k"], FAKE["v"],
+                               FAKE["y"], FAKE["ws"], ws, None)
+        assert st == INV
+
+
+def test_encode_and_decode_seams_validate():
+    L = lib()
+    ws = fp.flare_encode_workspace_size(2, 2, 128, 16, 8, 1, 64)
+    # q_batch_stride must be 0 or H*M*D
+    assert L.flare_encode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 5, FAKE["k"], FAKE["v"],
+                              FAKE["z"], 64, FAKE["ws"], ws, None) == INV
+    # chunk not a multiple of 64
+    assert L.flare_encode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 0, FAKE["k"], FAKE["v"],
+                              FAKE["z"], 96, FAKE["ws"], ws, None) == INV
+    # z aliasing k
+    assert L.flare_encode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 0, FAKE["k"], FAKE["v"],
+                              FAKE["k"], 64, FAKE["ws"], ws, None) == INV
+    wsd = fp.flare_decode_workspace_size(2, 2, 128, 16, 8, 1)
+    assert L.flare_decode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 0, FAKE["z"], FAKE["k"],
+                              FAKE["k"], FAKE["ws"], wsd, None) == INV
+    assert L.flare_decode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 0, None, FAKE["k"],
+                              FAKE["y"], FAKE["ws"], wsd, None) == INV
