@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""FLARE++ mixer forward throughput on one MI355X.
+
+A step is one flarepp_mixer_fwd call (synthesis, gated query, encode,
+decode) over one batch of the million-token workload (B=1, H=8, N=1,048,576,
+M=512, D=32, bf16, seeded synthetic inputs already resident in HBM).
+Prints one JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--cpu-seconds S | --no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FLARE++ mixer fwd tokens/s & TFLOP/s (%bf16 MFMA peak), 1 GPU, N=1M M=512"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+KERNELS = ["prep_seeds", "encode_synthesis", "combine_query", "encode", "combine_value",
+           "decode"]
+COUNTER_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_million_token.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                        ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e: int):
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_latent_attention_mixer_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(w, sig_open):
+    """Per-launch algorithmic flops and HBM bytes of the three attention
+    kernels (exp and normalisation not counted; partials not counted)."""
+    e = 2 if w.dtype in ("bf16", "fp16") else 4
+    tok = w.B * w.N
+    per_head_flops = 4 * tok * w.M * w.D          # QK^T and PV, 2 flops per MAC
+    per_head_bytes = tok * w.D * e                # one pass over one [N, D] tensor
+    hopen = int(sum(sig_open))
+    return {
+        "encode_synthesis": (per_head_flops * hopen, per_head_bytes * hopen),       # k0 once
+        "encode": (per_head_flops * w.H, 2 * per_head_bytes * w.H),                # k, v
+        "decode": (per_head_flops * w.H, 2 * per_head_bytes * w.H),                # k in, y out
+    }
+
+
+def cpu_baseline(x, w, seconds):
+    """The fp64 oracle, timed on whole heads of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+    except Exception:  # noqa: BLE001
+        blas = []
+    threads = max([n for _, n in blas] + [1])
+    heads = 0
+    t_total = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = dict(q0=x["q0"][h:h + 1], q_fixed=x["q_fixed"][h:h + 1],
+                      gate=x["gate"][h:h + 1], k0=x["k0"][b:b + 1, h:h + 1],
+                      k=x["k"][b:b + 1, h:h + 1], v=x["v"][b:b + 1, h:h + 1])
+            sl = {n: np.asarray(a, dtype=np.float64) for n, a in sl.items()}
+            t0 = time.perf_counter()
+            oracle.flarepp_ref(**sl)
+            t_total += time.perf_counter() - t0
+            heads += 1
+            log(f"[cpu] oracle head (b={b}, h={h}) done, {t_total:.1f}s so far")
+            if t_total >= seconds:
+                break
+        if t_total >= seconds:
+            break
+    t_head = t_total / heads
+    tokens_per_s = (w.B * w.N) / (t_head * w.B * w.H)
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads (full N={w.N}) of {w.name}, fp64 NumPy, "
+                      f"{t_total:.1f}s; rate scaled to all heads",
+            "blas": blas}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="million_token_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}, WORLD_SIZE {world}); "
+              "the mixer is built and measured on a single MI355X", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import rank_latent_attention_mixer_amd as fp
+    from flarepp_workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        log("no GPU available")
+        return 1
+    fp.load_library()
+    w = WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
+    log(f"[bench] generating {w.name} {w.shape_dict} {w.dtype}")
+    t0 = time.perf_counter()
+    x = make_inputs(w)
+    d = {}
+    for n in ("q0", "q_fixed", "k0", "k", "v"):
+        d[n] = torch.from_numpy(x[n]).to(dev).to(tdt)
+    d["gate"] = torch.from_numpy(x["gate"]).to(dev)
+    y = torch.empty_like(d["k"])
+    code = fp.dtype_code(d["k"])
+    ws = torch.empty(fp.flarepp_workspace_size(w.B, w.H, w.N, w.M, w.D, code), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident ({time.perf_counter() - t0:.1f}s)")
+
+    args = (d["q0"], d["q_fixed"], d["gate"], d["k0"], d["k"], d["v"])
+    for _ in range(a.warmup):
+        fp.flarepp_mixer_fwd(*args, y=y, workspace=ws)
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    evs = [[hip.create() for _ in range(fp.FLAREPP_TIMED_EVENTS)] for _ in range(a.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(a.steps):
+        fp.flarepp_mixer_fwd_timed(*args, events=evs[i], y=y, workspace=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / a.steps
+    per_kernel = {}
+    for j, name in enumerate(KERNELS):
+        per_kernel[name] = sum(hip.elapsed_ms(e[j], e[j + 1]) for e in evs) / a.steps
+    for e in evs:
+        for h in e:
+            hip.destroy(h)
+    log("[bench] per-kernel ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_kernel.items()))
+
+    sig = 1.0 / (1.0 + np.exp(-x["gate"].astype(np.float64)))
+    sig_open = [s > 0 for s in sig]
+    flops = sum((12 if o else 8) for o in sig_open) * w.B * w.N * w.M * w.D
+    t = ms_per_step / 1e3
+    tokens_per_s = w.B * w.N / t
+    tflops = flops / t / 1e12
+
+    work = algorithmic_work(w, sig_open)
+    dom = max(work, key=lambda k: per_kernel[k])
+    f_launch, b_launch = work[dom]
+    dur = per_kernel[dom] / 1e3
+    achieved = f_launch / dur / 1e12
+    traffic = None
+    if os.path.exists(COUNTER_FILE):
+        with open(COUNTER_FILE) as fh:
+            cf = json.load(fh)
+        k = cf.get("kernels", {}).get(dom)
+        if k and cf.get("source_digest") == source_digest() and cf.get("workload") == w.name:
+            traffic = k["hbm_bytes_per_launch"]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": dom,
+                "algorithmic_flops_per_launch": f_launch,
+                "algorithmic_bytes_per_launch": b_launch,
+                "avg_launch_ms": round(per_kernel[dom], 4),
+                "achieved_algorithmic_GBs": round(b_launch / dur / 1e9, 1)}
+
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D,
+                   "dtype": w.dtype, "global_batch": w.B, "seq_len": w.N,
+                   "parallelism": "single-gpu"},
+        "tflops": round(tflops, 2),
+        "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x, w, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -119,6 +119,24 @@ int flarepp_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Same computation as flarepp_mixer_fwd, with timing marks for profiling.
+ * `events` points to FLAREPP_TIMED_EVENTS hipEvent_t handles created by the
+ * caller; the call records them on `stream` around its launches:
+ *   events[0] start                      events[1] after the seed operand copy
+ *   events[2] after the synthesis encoder events[3] after the gated combine
+ *   events[4] after the encoder          events[5] after the value combine
+ *   events[6] after the decoder
+ * so that elapsed(events[i], events[i+1]) is the duration of one kernel.
+ * Errors as for flarepp_mixer_fwd; events == NULL is INVALID_ARGUMENT.
+ */
+#define FLAREPP_TIMED_EVENTS 7
+int flarepp_mixer_fwd_timed(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                            const void* q0, const void* q_fixed, const float* gate,
+                            const void* k0, const void* k, const void* v, void* y,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events);
+
+/*
  * Two-step FLARE mixer forward (FLARE.py README, section "FLARE"):
  *   z = softmax_rows(scale q k^T) v ;  y = softmax_rows(scale k q^T) z.
  * The listing on that page uses scale = 1.0; a closed-gate FLARE++ head

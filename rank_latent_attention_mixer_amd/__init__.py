@@ -24,7 +24,7 @@ import re
 
 __all__ = [
     "FlareppError", "load_library", "library_path", "dtype_code",
-    "flarepp_mixer_fwd", "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
+    "flarepp_mixer_fwd", "flarepp_mixer_fwd_timed", "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
     "flarepp_workspace_size", "flare_encode_workspace_size", "flare_decode_workspace_size",
     "flarepp_status_string", "flarepp_version", "declared_functions",
     "FLAREPP_OK", "FLAREPP_ERR_INVALID_ARGUMENT", "FLAREPP_ERR_UNSUPPORTED",
@@ -80,6 +80,8 @@ def load_library():
     lib.flare_decode_workspace_size.restype = sz
     lib.flarepp_mixer_fwd.argtypes = shape + [i32] + [vp] * 7 + [vp, sz, vp]
     lib.flarepp_mixer_fwd.restype = i32
+    lib.flarepp_mixer_fwd_timed.argtypes = shape + [i32] + [vp] * 7 + [vp, sz, vp, vp]
+    lib.flarepp_mixer_fwd_timed.restype = i32
     lib.flare_mixer_fwd.argtypes = shape + [i32, f32] + [vp] * 4 + [vp, sz, vp]
     lib.flare_mixer_fwd.restype = i32
     lib.flare_encode_fwd.argtypes = shape + [i32, f32, vp, i64, vp, vp, vp, i64, vp, sz, vp]
@@ -191,6 +193,40 @@ def flarepp_mixer_fwd(q0, q_fixed, gate, k0, k, v, y=None, workspace=None, strea
     _call(lib.flarepp_mixer_fwd, "flarepp_mixer_fwd", B, H, N, M, D, code, _ptr(q0),
           _ptr(q_fixed), _ptr(gate), _ptr(k0), _ptr(k), _ptr(v), _ptr(y), _ptr(ws),
           ws.numel(), _stream(stream))
+    return y
+
+
+FLAREPP_TIMED_EVENTS = 7
+
+
+def flarepp_mixer_fwd_timed(q0, q_fixed, gate, k0, k, v, events, y=None, workspace=None,
+                            stream=None):
+    """flarepp_mixer_fwd recording FLAREPP_TIMED_EVENTS caller-created
+    hipEvent_t handles (integers) on the stream around its kernels."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q0.shape[1]
+    dev, dt = k.device, k.dtype
+    for name, t, shp in (("q0", q0, (H, M, D)), ("q_fixed", q_fixed, (H, M, D)),
+                         ("k0", k0, (B, H, N, D)), ("k", k, (B, H, N, D)),
+                         ("v", v, (B, H, N, D))):
+        _check_tensor(name, t, shp, dt, dev)
+    _check_tensor("gate", gate, (H,), torch.float32, dev)
+    if len(events) != FLAREPP_TIMED_EVENTS:
+        raise ValueError(f"need {FLAREPP_TIMED_EVENTS} events")
+    if y is None:
+        y = torch.empty((B, H, N, D), dtype=dt, device=dev)
+    _check_tensor("y", y, (B, H, N, D), dt, dev)
+    code = dtype_code(k)
+    nbytes = lib.flarepp_workspace_size(B, H, N, M, D, code)
+    if nbytes == 0:
+        raise FlareppError(FLAREPP_ERR_UNSUPPORTED, "flarepp_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    ev = (ctypes.c_void_p * FLAREPP_TIMED_EVENTS)(*[ctypes.c_void_p(e) for e in events])
+    _call(lib.flarepp_mixer_fwd_timed, "flarepp_mixer_fwd_timed", B, H, N, M, D, code,
+          _ptr(q0), _ptr(q_fixed), _ptr(gate), _ptr(k0), _ptr(k), _ptr(v), _ptr(y), _ptr(ws),
+          ws.numel(), _stream(stream), ev)
     return y
 
 

@@ -49,13 +49,6 @@ __device__ __forceinline__ float merged_value(const CombineParams& a, int set, i
   return O / L;
 }
 
-// Row of the decoder's value operand that holds output column d, for NDB
-// 16-row blocks: block b, row rho holds column (rho/4)*(4*NDB) + 4*b + rho%4.
-__device__ __forceinline__ int value_row_of(int d, int ndb) {
-  const int grp = d / (4 * ndb), rem = d - grp * 4 * ndb;
-  const int blk = rem >> 2, i = rem & 3;
-  return 16 * blk + 4 * grp + i;
-}
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
   const int set = blockIdx.y;
@@ -87,7 +80,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
     }
   }
   if (a.out_kind == kOutValueT) {
-    const int row = d < a.D ? value_row_of(d, a.DV / 16) : d;  // padded rows stay in place
+    const int row = (d & ~31) + value_row(d & 31);  // padded columns map to zero rows
     const int col = (m & ~31) + key_slot(m & 31);
     store_from_float(a.out, ((int64_t)set * a.DV + row) * a.Mpad + col, a.out_dtype, val);
   } else {

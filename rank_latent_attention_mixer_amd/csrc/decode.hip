@@ -5,7 +5,7 @@
 // The latents of one (batch, head) -- routing queries q as keys and encoded
 // values z as values -- are loaded into LDS once per workgroup and stay
 // resident while the workgroup walks its token tiles (persistent over
-// tiles).  Tokens are the register side: each wave takes 64 tokens, loads
+// tiles).  Tokens are the register side: each wave takes 32 * kNC tokens, loads
 // their k rows straight from HBM into matrix-core operands, sweeps the
 // latents 32 at a time with the shared online-softmax tile, and writes its
 // normalised y rows.  The value operand arrives with permuted rows so that
@@ -17,20 +17,30 @@ namespace flarepp {
 
 namespace {
 
-constexpr int kNC = 4;       // 16-token column blocks per wave
-constexpr int kNW = 8;       // waves per workgroup
-constexpr int kTokTile = 64 * kNW;
+// 32-token column blocks per wave and waves per workgroup (build-time knobs)
+#ifndef FLAREPP_DEC_NC
+#define FLAREPP_DEC_NC 1
+#endif
+constexpr int kNC = FLAREPP_DEC_NC;
+// waves per workgroup: 16 (four per SIMD) where the registers allow it
+template <int D>
+struct DecodeWaves {
+  static constexpr int value = 8;
+};
 
 template <int D>
 struct DecodeLds {
-  static constexpr int DV = D < 16 ? 16 : D;
-  static constexpr int KP = (D < 8 ? 8 : D) + 8;  // latent row pitch (elements)
+  static constexpr int DV = D < 32 ? 32 : D;
+  static constexpr int KP = D + 8;  // latent row pitch (elements)
   static int zpitch(int Mk) { return Mk + 8; }
   static int elems(int Mk) { return Mk * KP + DV * zpitch(Mk); }
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(64 * kNW) void decode_kernel(DecodeParams a) {
+__global__ __launch_bounds__(64 * DecodeWaves<D>::value) void
+decode_kernel(DecodeParams a) {
+  constexpr int kNW = DecodeWaves<D>::value;
+  constexpr int kTokTile = 32 * kNC * kNW;
   using Tile = FlashTile<T, D, kNC>;
   using V8 = typename Tile::V8;
   constexpr int KD = Tile::KD, DV = Tile::DV, NDB = Tile::NDB;
@@ -44,14 +54,14 @@ __global__ __launch_bounds__(64 * kNW) void decode_kernel(DecodeParams a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r = lane & 15;
+  const int h = lane >> 5, r = lane & 31;
   const int bh = blockIdx.x / a.wg_per_bh;
   const int part = blockIdx.x - bh * a.wg_per_bh;
-  const int b = bh / a.H, h = bh - b * a.H;
+  const int b = bh / a.H, hd = bh - b * a.H;
 
   // resident latents: q rows [0, Mk) and the value operand rows [0, DV)
   {
-    const T* qg = reinterpret_cast<const T*>(a.q) + b * a.q_b_stride + h * a.q_h_stride;
+    const T* qg = reinterpret_cast<const T*>(a.q) + b * a.q_b_stride + hd * a.q_h_stride;
     constexpr int G8 = D / 8;
     for (int u = tid; u < Mk * G8; u += 64 * kNW) {
       const int row = u / G8, e = u - row * G8;
@@ -69,60 +79,152 @@ __global__ __launch_bounds__(64 * kNW) void decode_kernel(DecodeParams a) {
   const T* kg = reinterpret_cast<const T*>(a.k) + (int64_t)bh * a.N * D;
   T* yg = reinterpret_cast<T*>(a.y) + (int64_t)bh * a.N * D;
   const int64_t ntiles = (a.N + kTokTile - 1) / kTokTile;
-  const int nkt = Mk / 32;
+  const int nfull = a.M / 32, mtail = a.M - 32 * nfull;
+
+  // lane-constant byte offsets of the resident operands; a latent group G
+  // adds G * (32 rows) to the key operand and G * (32 slots) to the values
+  int kl[KD];
+#pragma unroll
+  for (int kd = 0; kd < KD; ++kd) kl[kd] = (r * KP + 16 * kd + 8 * h) * (int)sizeof(T);
+  int vl[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) vl[db] = ((32 * db + r) * ZP + 8 * h) * (int)sizeof(T);
+  const unsigned char* qsb = reinterpret_cast<const unsigned char*>(qs);
+  const unsigned char* zsb = reinterpret_cast<const unsigned char*>(zs);
+  constexpr int KSTEP = 32 * KP * (int)sizeof(T);  // bytes per latent group, key operand
+  constexpr int VSTEP = 32 * (int)sizeof(T);       // bytes per latent group, value operand
+  auto kop_at = [&](int G, V8 (&kop)[KD]) {
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) {
+      if (16 * kd + 8 * h < D)
+        kop[kd] = *reinterpret_cast<const V8*>(qsb + kl[kd] + G * KSTEP);
+      else
+        kop[kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+    }
+  };
+  auto vop_at = [&](int G, V8 (&vop)[NDB][2]) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        vop[db][kk] =
+            *reinterpret_cast<const V8*>(zsb + vl[db] + G * VSTEP + kk * 16 * (int)sizeof(T));
+  };
 
   for (int64_t tile = part; tile < ntiles; tile += a.wg_per_bh) {
-    const int64_t nb = tile * kTokTile + wave * 64;
+    const int64_t nb = tile * kTokTile + wave * 32 * kNC;
     if (nb >= a.N) continue;  // wave-uniform; no barrier below
     Tile st;
     st.reset();
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
-      const int64_t n = nb + cb * 16 + r;
+      const int64_t n = nb + cb * 32 + r;
 #pragma unroll
       for (int kd = 0; kd < KD; ++kd) {
-        const int d0 = 32 * kd + 8 * g;
+        const int d0 = 16 * kd + 8 * h;
         if (d0 < D && n < a.N) st.q[cb][kd] = bitcast_u4<V8>(ldg16(kg + n * D + d0));
         else st.q[cb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
       }
     }
-    for (int kt = 0; kt < nkt; ++kt) {
-      V8 kop[2][KD];
-      V8 vop[NDB];
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int kd = 0; kd < KD; ++kd) {
-          const int d0 = 32 * kd + 8 * g;
-          if (d0 < D)
-            kop[jb][kd] = *reinterpret_cast<const V8*>(&qs[(32 * kt + 16 * jb + r) * KP + d0]);
-          else
-            kop[jb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
-        }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        vop[db] = *reinterpret_cast<const V8*>(&zs[(16 * db + r) * ZP + 32 * kt + 8 * g]);
-      st.step(kop, vop, min(32, a.M - 32 * kt), g);
+    // latent groups of 32: group 0 sets the references, full groups run as
+    // a two-stage pipeline (two score buffers alternating), then a masked
+    // tail group
+    f32x16 sa[kNC], sb[kNC];
+    {
+      V8 kop[KD];
+      kop_at(0, kop);
+      st.scores(kop, sa);
+      V8 vop[NDB][2];
+      vop_at(0, vop);
+      if (nfull > 0) st.template first<false>(sa, vop, 32, h);
+      else st.template first<true>(sa, vop, mtail, h);
     }
-    // y = O / l; lane (g, r) owns columns [g*4*NDB, (g+1)*4*NDB) of token r
+    if (nfull > 1) {
+      {
+        V8 kop[KD];
+        kop_at(1, kop);
+        st.scores(kop, sa);
+      }
+      for (int G = 1; G < nfull; G += 2) {
+        const bool more = G + 1 < nfull;
+        if (more) {
+          V8 kop[KD];
+          kop_at(G + 1, kop);
+          st.scores(kop, sb);
+        }
+        {
+          V8 vop[NDB][2];
+          vop_at(G, vop);
+          st.template next<false>(sa, vop, 32, h);
+        }
+        if (!more) break;
+        if (G + 2 < nfull) {
+          V8 kop[KD];
+          kop_at(G + 2, kop);
+          st.scores(kop, sa);
+        }
+        V8 vop[NDB][2];
+        vop_at(G + 1, vop);
+        st.template next<false>(sb, vop, 32, h);
+      }
+    }
+    if (nfull > 0 && mtail > 0) {
+      V8 kop[KD];
+      kop_at(nfull, kop);
+      st.scores(kop, sa);
+      V8 vop[NDB][2];
+      vop_at(nfull, vop);
+      st.template next<true>(sa, vop, mtail, h);
+    }
+    // fixed references overflowed: exact two-pass recompute of this wave's
+    // tokens (true maxima over all latents first, then the sums)
+    if (st.overflowed()) {
+      const int ngrp = nfull + (mtail > 0 ? 1 : 0);
+      float mx[kNC];
+#pragma unroll
+      for (int cb = 0; cb < kNC; ++cb) mx[cb] = -__builtin_inff();
+      st.reset();
+      for (int G = 0; G < ngrp; ++G) {
+        V8 kop[KD];
+        kop_at(G, kop);
+        st.scores(kop, sa);
+        Tile::mask(sa, a.M - 32 * G, h);
+        float gm[kNC];
+        Tile::colmax(sa, gm);
+#pragma unroll
+        for (int cb = 0; cb < kNC; ++cb) mx[cb] = fmaxf(mx[cb], gm[cb]);
+      }
+      st.set_reference(sa, mx);
+      for (int G = 0; G < ngrp; ++G) {
+        V8 kop[KD];
+        kop_at(G, kop);
+        st.scores(kop, sa);
+        V8 vop[NDB][2];
+        vop_at(G, vop);
+        st.template next<true>(sa, vop, a.M - 32 * G, h);
+      }
+    }
+    // y = O / l; lane (h, r) owns columns 32db + 16h .. +15 of token r
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
       const float inv = 1.0f / st.row_sum(cb);
-      const int64_t n = nb + cb * 16 + r;
-      const int d0 = g * 4 * NDB;
-      if (n < a.N && d0 < D) {
-        T out[4 * NDB];
+      const int64_t n = nb + cb * 32 + r;
+      if (n < a.N) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db) {
+          const int d0 = 32 * db + 16 * h;
+          if (d0 < D) {
+            T out[16];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) out[4 * db + i] = (T)(st.o[db][cb][i] * inv);
-        T* dst = yg + n * D + d0;
-        if constexpr (4 * NDB * sizeof(T) >= 16) {
-#pragma unroll
-          for (int w = 0; w < (int)(4 * NDB * sizeof(T)) / 16; ++w)
-            *reinterpret_cast<u32x4*>(dst + w * 8) = *reinterpret_cast<const u32x4*>(&out[w * 8]);
-        } else {
-          *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(&out[0]);
+            for (int v = 0; v < 16; ++v) out[v] = (T)(st.o[db][cb][v] * inv);
+            T* dst = yg + n * D + d0;
+            if constexpr (D >= 16) {
+              *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
+              *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(&out[8]);
+            } else {
+              *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
+            }
+          }
         }
       }
     }
@@ -202,7 +304,7 @@ hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(p.B * p.H * p.wg_per_bh));
-  hipLaunchKernelGGL((decode_kernel<T, D>), grid, dim3(64 * kNW), lds, s, p);
+  hipLaunchKernelGGL((decode_kernel<T, D>), grid, dim3(64 * DecodeWaves<D>::value), lds, s, p);
   return hipGetLastError();
 }
 
@@ -225,6 +327,10 @@ hipError_t launch_f32(const DecodeParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int decode_tokens_per_tile(int D) {
+  return 32 * kNC * (D >= 64 ? DecodeWaves<64>::value : DecodeWaves<32>::value);
+}
 
 int decode_lds_bytes(int M, int D, int dtype) {
   if (dtype == kF32) return 0;

@@ -6,12 +6,12 @@
 // "Multi-GPU context parallelism": exact token-sharded encoder).
 //
 // One workgroup = one (batch, head, token chunk).  Its waves split the
-// latents (64 per wave); every wave consumes the same K/V tiles, staged in
-// LDS once per workgroup: K in natural [token][d] layout, V transposed to
-// [d][key slot] while it is written (the P.V product contracts over tokens,
-// so the matrix-core operand needs V with tokens along k).  Tiles of 64
-// tokens are double-buffered: the global loads of tile t+1 are in flight
-// while tile t is computed.
+// latents (32 * kNC per wave); every wave consumes the same K/V tiles, which
+// are staged in LDS in their natural [token][d] layout.  The P.V product contracts over tokens, so
+// its matrix-core operand needs V with tokens along k: it is read with the
+// transposing LDS load (ds_read_b64_tr_b16) instead of being transposed in
+// flight.  Tiles of 64 tokens rotate over three LDS buffers; the loads of
+// tile t+1 are in flight while tile t is computed.
 #include "flash_tile.hpp"
 #include "kernels.hpp"
 
@@ -19,162 +19,331 @@ namespace flarepp {
 
 namespace {
 
-constexpr int kNC = 4;        // 16-column blocks per wave -> 64 latents per wave
+// 32-column blocks per wave (build-time knob; 1 keeps the register
+// footprint low enough for four waves per SIMD)
+#ifndef FLAREPP_ENC_NC
+#define FLAREPP_ENC_NC 1
+#endif
+constexpr int kNC = FLAREPP_ENC_NC;
+constexpr int kMaxWaves = 16 / kNC;   // waves per workgroup for M = 512
 constexpr int kTJ = 64;       // tokens per LDS tile
+constexpr int kGPT = kTJ / 32;  // 32-key groups per tile
+// LDS tiles rotate over three buffers: with the score product running one
+// group ahead, a wave may still read tile t-1 while others fill tile t+1.
+constexpr int kNBUF = 3;
+
+// LDS tile layout: token rows of 2*D bytes in natural [token][d] order, the
+// 16-byte chunks of row `row` XOR-permuted by swz(row) so that both the
+// K-operand reads (16 rows x 16 bytes per phase) and the transposing V reads
+// hit distinct banks.
+template <int D>
+struct TileLayout {
+  static constexpr int ROWB = 2 * D;           // bytes per token row
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int RPB = 256 / ROWB;       // rows per 256 bytes (all banks)
+  static constexpr int TILEB = kTJ * ROWB;     // bytes per tile per tensor
+  __device__ __forceinline__ static int swz(int row) { return (row / RPB) % CPR; }
+  __device__ __forceinline__ static int offset(int row, int byte) {  // byte within row
+    return row * ROWB + (((byte >> 4) ^ swz(row)) << 4) + (byte & 15);
+  }
+};
 
 template <typename T, int D, int NW, bool SHARED_KV>
 __global__ __launch_bounds__(64 * NW) void encode_split_kernel(EncodeParams a) {
   using Tile = FlashTile<T, D, kNC>;
   using V8 = typename Tile::V8;
-  constexpr int KD = Tile::KD, DV = Tile::DV, NDB = Tile::NDB;
-  constexpr int KP = (D < 8 ? 8 : D) + 8;   // K row pitch (elements), 16-byte multiple
-  constexpr int VP = kTJ + 8;               // V^T row pitch
-  constexpr int NT = 64 * NW;
-  constexpr int G8 = D / 8;                 // 16-byte groups per token row
-  constexpr int U = (kTJ / 2) * G8;         // load units per tile: 2 rows x 16 bytes
-  constexpr int UPT = (U + NT - 1) / NT;
+  using L = TileLayout<D>;
+  constexpr int KD = Tile::KD, NDB = Tile::NDB;
+  constexpr int NTEN = SHARED_KV ? 1 : 2;               // tensors staged per tile
+  constexpr int LOADS = L::TILEB / 1024;                // 1 KB wave loads per tensor
+  static_assert(L::TILEB % 1024 == 0, "tile must be a whole number of wave loads");
 
-  __shared__ __attribute__((aligned(16))) T ks[2][kTJ * KP];
-  __shared__ __attribute__((aligned(16))) T vt[2][DV * VP];
+  // Three tile buffers as three distinct LDS objects: reads from one buffer
+  // then provably do not alias the direct loads landing in another, so the
+  // compiler does not make them wait for those loads.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[NTEN * L::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[NTEN * L::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char lds2[NTEN * L::TILEB];
+  auto buf_c = [&](auto bc) -> unsigned char* {
+    constexpr int B = decltype(bc)::value;
+    if constexpr (B == 0) return lds0;
+    else if constexpr (B == 1) return lds1;
+    else return lds2;
+  };
+  auto buf_rt = [&](int b) -> unsigned char* { return b == 0 ? lds0 : b == 1 ? lds1 : lds2; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r = lane & 15;
+  const int h = lane >> 5, r = lane & 31;
   const int bh = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x - bh * a.nchunks;
-  const int b = bh / a.H, h = bh - b * a.H;
+  const int b = bh / a.H, hd = bh - b * a.H;
 
-  if (a.gate != nullptr && gate_sigma(a.gate[h]) == 0.f) return;  // closed gate: no synthesis
+  if (a.gate != nullptr && gate_sigma(a.gate[hd]) == 0.f) return;  // closed gate: no synthesis
 
   const int64_t n0 = (int64_t)chunk * a.chunk_tokens;
   const int64_t n1 = min(a.N, n0 + a.chunk_tokens);
-  const int ntiles = (int)((n1 - n0 + kTJ - 1) / kTJ);
+  const int ntok = (int)(n1 - n0);
+  const int ntiles = (ntok + kTJ - 1) / kTJ;
   const T* kbase = reinterpret_cast<const T*>(a.k) + (int64_t)bh * a.N * D;
   const T* vbase = reinterpret_cast<const T*>(a.v) + (int64_t)bh * a.N * D;
-
-  if constexpr (D < 16) {
-    // value rows D..15 of both buffers stay zero for the whole kernel
-    for (int e = tid; e < 2 * (DV - D) * VP; e += NT) {
-      const int buf = e / ((DV - D) * VP), rem = e - buf * (DV - D) * VP;
-      vt[buf][D * VP + rem] = (T)0.f;
-    }
-  }
 
   Tile st;
   st.reset();
   {
-    const T* qb = reinterpret_cast<const T*>(a.q) + b * a.q_b_stride + h * a.q_h_stride;
+    const T* qb = reinterpret_cast<const T*>(a.q) + b * a.q_b_stride + hd * a.q_h_stride;
+    const int col = wave * 32 * kNC + r;
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
-      const int col = wave * 16 * kNC + cb * 16 + r;
 #pragma unroll
       for (int kd = 0; kd < KD; ++kd) {
-        const int d0 = 32 * kd + 8 * g;
-        if (d0 < D) st.q[cb][kd] = bitcast_u4<V8>(ldg16(qb + (int64_t)col * D + d0));
+        const int d0 = 16 * kd + 8 * h;
+        if (d0 < D) st.q[cb][kd] = bitcast_u4<V8>(ldg16(qb + (int64_t)(col + 32 * cb) * D + d0));
         else st.q[cb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
       }
     }
   }
 
-  u32x4 pk[UPT][2], pv[UPT][2];
-  auto load_tile = [&](int t) {
-    const int64_t tb = n0 + (int64_t)t * kTJ;
-#pragma unroll
-    for (int uu = 0; uu < UPT; ++uu) {
-      const int u = tid + uu * NT;
-      if (U % NT == 0 || u < U) {
-        const int pr = u / G8, e = u - pr * G8;
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          const int64_t n = tb + 2 * pr + rr;
-          if (n < n1) {
-            pk[uu][rr] = ldg16(kbase + n * D + 8 * e);
-            if constexpr (!SHARED_KV) pv[uu][rr] = ldg16(vbase + n * D + 8 * e);
-          } else {
-            pk[uu][rr] = u32x4{0u, 0u, 0u, 0u};
-            if constexpr (!SHARED_KV) pv[uu][rr] = u32x4{0u, 0u, 0u, 0u};
-          }
-        }
-      }
+  // HBM -> LDS with no registers: a wave load moves 1 KB, lane i's 16 bytes
+  // landing at byte 16*i of it.  Rows past the chunk end re-read the chunk's
+  // last token (finite data; those keys are masked to probability 0).
+  auto issue_loads = [&](unsigned char* dst, int t) {
+    const int lim = ntok - 1 - t * kTJ;  // last valid row of the tile
+    const T* kt = kbase + (n0 + (int64_t)t * kTJ) * D;
+    const T* vt = vbase + (n0 + (int64_t)t * kTJ) * D;
+    for (int ld = wave; ld < NTEN * LOADS; ld += NW) {
+      const int ten = ld / LOADS, li = ld - ten * LOADS;
+      const int o = li * 1024 + 16 * lane;
+      const int row = o / L::ROWB;
+      const int clog = ((o % L::ROWB) >> 4) ^ L::swz(row);
+      const int eoff = min(row, lim) * D + 8 * clog;
+      global_to_lds16((ten == 0 ? kt : vt) + eoff, dst + ten * L::TILEB + li * 1024);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int uu = 0; uu < UPT; ++uu) {
-      const int u = tid + uu * NT;
-      if (U % NT == 0 || u < U) {
-        const int pr = u / G8, e = u - pr * G8;
-        const int j0 = 2 * pr;
-        *reinterpret_cast<u32x4*>(&ks[buf][j0 * KP + 8 * e]) = pk[uu][0];
-        *reinterpret_cast<u32x4*>(&ks[buf][(j0 + 1) * KP + 8 * e]) = pk[uu][1];
-        const u32x4 w0 = SHARED_KV ? pk[uu][0] : pv[uu][0];
-        const u32x4 w1 = SHARED_KV ? pk[uu][1] : pv[uu][1];
-        const int col = (j0 & ~31) + key_slot(j0 & 31);   // even; j0+1 lands at col+1
-        unsigned int* vrow = reinterpret_cast<unsigned int*>(&vt[buf][0]);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const unsigned int lo = (w0[qq] & 0xFFFFu) | (w1[qq] << 16);
-          const unsigned int hi = (w0[qq] >> 16) | (w1[qq] & 0xFFFF0000u);
-          const int d = 8 * e + 2 * qq;
-          vrow[(d * VP + col) >> 1] = lo;
-          vrow[((d + 1) * VP + col) >> 1] = hi;
-        }
-      }
-    }
+  // Entering tile t (buffer B = t % 3): its loads, issued one tile earlier,
+  // are complete in every wave after the barrier, which also retires all
+  // reads of tile t-2 -- whose buffer then receives tile t+1.
+  auto enter_tile = [&](auto bc, int t) {
+    constexpr int B = decltype(bc)::value;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntiles) issue_loads(buf_c(IntC<(B + 1) % kNBUF>{}), t + 1);
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const int tvalid = (int)min((int64_t)kTJ, n1 - (n0 + (int64_t)t * kTJ));
+  // Lane-constant parts of the LDS operand addresses.  The swizzle of a row
+  // only depends on the row's position within its 32-key group, so a group
+  // adds an immediate.
+  int kaddr[KD];
 #pragma unroll
-    for (int half = 0; half < kTJ / 32; ++half) {
-      const int kvalid = min(32, tvalid - 32 * half);
-      if (kvalid > 0) {
-        V8 kop[2][KD];
-        V8 vop[NDB];
+  for (int kd = 0; kd < KD; ++kd) kaddr[kd] = L::offset(r, 2 * (16 * kd + 8 * h));
+  // V^T operand through the transposing LDS read: in each 16-lane group,
+  // source lane 4k+q addresses key k, columns d0+4q..d0+4q+3, and lane j
+  // receives column d0+j of keys 0..3.
+  const int tr_k = (lane & 15) >> 2, tr_q = lane & 3;
+  int vaddr[NDB][2];
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+  for (int db = 0; db < NDB; ++db) {
+    int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * tr_q;
+    if (d >= D) d = 0;  // feeds only padded output rows
 #pragma unroll
-          for (int kd = 0; kd < KD; ++kd) {
-            const int d0 = 32 * kd + 8 * g;
-            if (d0 < D)
-              kop[jb][kd] = *reinterpret_cast<const V8*>(
-                  &ks[buf][(32 * half + 16 * jb + r) * KP + d0]);
-            else
-              kop[jb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
-          }
+    for (int aa = 0; aa < 2; ++aa)
+      vaddr[db][aa] = (NTEN - 1) * L::TILEB + L::offset(8 * aa + 4 * h + tr_k, 2 * d);
+  }
+  auto kop_at = [&](const unsigned char* base, int grp, V8 (&kop)[KD]) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          vop[db] = *reinterpret_cast<const V8*>(&vt[buf][(16 * db + r) * VP + 32 * half + 8 * g]);
-        st.step(kop, vop, kvalid, g);
-      }
+    for (int kd = 0; kd < KD; ++kd) {
+      if (16 * kd < D && (D >= 16 || h == 0))
+        kop[kd] = *reinterpret_cast<const V8*>(base + kaddr[kd] + grp * 32 * L::ROWB);
+      else
+        kop[kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+  };
+  auto vop_at = [&](const unsigned char* base, int grp, V8 (&vop)[NDB][2]) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        short4v part[2];
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+          part[aa] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4v*)(base + vaddr[db][aa] +
+                                                           (32 * grp + 16 * kk) * L::ROWB));
+        vop[db][kk] = __builtin_bit_cast(V8, short8v{part[0][0], part[0][1], part[0][2], part[0][3],
+                                                     part[1][0], part[1][1], part[1][2], part[1][3]});
+      }
+  };
+
+  // Key groups of 32 tokens, two per 64-token tile.  Tile 0 runs plainly
+  // (its first group sets the references).  Full tiles 1 .. nft-1 run as a
+  // two-stage pipeline -- the score product of the next group is issued
+  // before the softmax of the current one, two score buffers alternating --
+  // with the buffer rotation unrolled so every LDS address is a lane base
+  // plus an immediate.  A partial last tile follows.
+  const int nft = ntok / kTJ;  // full tiles
+  f32x16 sa[kNC], sb[kNC];
+  issue_loads(lds0, 0);
+  enter_tile(IntC<0>{}, 0);
+  {
+    V8 kop[KD];
+    kop_at(lds0, 0, kop);
+    st.scores(kop, sa);
+    V8 vop[NDB][2];
+    vop_at(lds0, 0, vop);
+    if (ntok >= 32) st.template first<false>(sa, vop, 32, h);
+    else st.template first<true>(sa, vop, ntok, h);
+  }
+  if (ntok > 32) {
+    V8 kop[KD];
+    kop_at(lds0, 1, kop);
+    st.scores(kop, sa);
+    V8 vop[NDB][2];
+    vop_at(lds0, 1, vop);
+    if (ntok >= 64) st.template next<false>(sa, vop, 32, h);
+    else st.template next<true>(sa, vop, ntok - 32, h);
+  }
+  // tile t in buffer B whose successor t+1 is also full; on entry sa holds
+  // the scores of tile t's first group, on exit those of tile t+1's
+  auto tile_body = [&](auto bc, int t) {
+    constexpr int B = decltype(bc)::value, BN = (B + 1) % kNBUF;
+    const unsigned char* cur = buf_c(bc);
+    {
+      V8 kop[KD];
+      kop_at(cur, 1, kop);
+      st.scores(kop, sb);
+      V8 vop[NDB][2];
+      vop_at(cur, 0, vop);
+      st.template next<false>(sa, vop, 32, h);
+    }
+    enter_tile(IntC<BN>{}, t + 1);
+    V8 kop[KD];
+    kop_at(buf_c(IntC<BN>{}), 0, kop);
+    st.scores(kop, sa);
+    V8 vop[NDB][2];
+    vop_at(cur, 1, vop);
+    st.template next<false>(sb, vop, 32, h);
+  };
+  if (nft > 1) {
+    enter_tile(IntC<1>{}, 1);
+    {
+      V8 kop[KD];
+      kop_at(lds1, 0, kop);
+      st.scores(kop, sa);
+    }
+    int t = 1;
+    while (true) {  // every tile entered here is followed by a full one
+      if (t + 1 >= nft) break;
+      tile_body(IntC<1>{}, t++);
+      if (t + 1 >= nft) break;
+      tile_body(IntC<2>{}, t++);
+      if (t + 1 >= nft) break;
+      tile_body(IntC<0>{}, t++);
+    }
+    // last full tile, t = nft - 1
+    const unsigned char* cur = buf_rt(t % kNBUF);
+    V8 kop[KD];
+    kop_at(cur, 1, kop);
+    st.scores(kop, sb);
+    V8 vop[NDB][2];
+    vop_at(cur, 0, vop);
+    st.template next<false>(sa, vop, 32, h);
+    vop_at(cur, 1, vop);
+    st.template next<false>(sb, vop, 32, h);
+  }
+  // the partial last tile (1..63 tokens) after full ones
+  const int rem = ntok - nft * kTJ;
+  if (nft > 0 && rem > 0) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    const unsigned char* cur = buf_rt(nft % kNBUF);
+    for (int grp = 0; grp * 32 < rem; ++grp) {
+      const int kvalid = min(32, rem - 32 * grp);
+      V8 kop[KD];
+      kop_at(cur, grp, kop);
+      st.scores(kop, sa);
+      V8 vop[NDB][2];
+      vop_at(cur, grp, vop);
+      if (kvalid == 32) st.template next<false>(sa, vop, 32, h);
+      else st.template next<true>(sa, vop, kvalid, h);
+    }
+  }
+
+  // The fixed references overflowed (scores far above the first group's
+  // maximum): recompute this wave's columns exactly, straight from HBM --
+  // first the true column maxima, then the sums, where nothing can exceed 1.
+  if (st.overflowed()) {
+    auto kop_g = [&](int G, V8 (&kop)[KD]) {
+      const int tok = min(32 * G + r, ntok - 1);
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) {
+        const int d0 = 16 * kd + 8 * h;
+        if (d0 < D) kop[kd] = bitcast_u4<V8>(ldg16(kbase + (n0 + tok) * D + d0));
+        else kop[kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+      }
+    };
+    auto vop_g = [&](int G, V8 (&vop)[NDB][2]) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + r;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          V8 x;
+#pragma unroll
+          for (int t8 = 0; t8 < 8; ++t8) {
+            const int tok = min(32 * G + 16 * kk + 8 * (t8 >> 2) + 4 * h + (t8 & 3), ntok - 1);
+            x[t8] = d < D ? vbase[(n0 + tok) * D + d] : (T)0.f;
+          }
+          vop[db][kk] = x;
+        }
+      }
+    };
+    const int ngrp = (ntok + 31) / 32;
+    float mx[kNC];
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb) mx[cb] = -__builtin_inff();
+    st.reset();
+    for (int G = 0; G < ngrp; ++G) {
+      V8 kop[KD];
+      kop_g(G, kop);
+      st.scores(kop, sa);
+      Tile::mask(sa, ntok - 32 * G, h);
+      float gm[kNC];
+      Tile::colmax(sa, gm);
+#pragma unroll
+      for (int cb = 0; cb < kNC; ++cb) mx[cb] = fmaxf(mx[cb], gm[cb]);
+    }
+    st.set_reference(sa, mx);
+    for (int G = 0; G < ngrp; ++G) {
+      V8 kop[KD];
+      kop_g(G, kop);
+      st.scores(kop, sa);
+      V8 vop[NDB][2];
+      vop_g(G, vop);
+      st.template next<true>(sa, vop, ntok - 32 * G, h);
+    }
   }
 
   // partials of this chunk
   const int64_t base = ((int64_t)bh * a.nchunks + chunk) * a.Mpad;
 #pragma unroll
   for (int cb = 0; cb < kNC; ++cb) {
-    const int col = wave * 16 * kNC + cb * 16 + r;
+    const int col = wave * 32 * kNC + cb * 32 + r;
     const float lt = st.row_sum(cb);
-    if (g == 0) {
+    if (h == 0) {
       a.part_m[base + col] = -st.negm[cb][0];
       a.part_l[base + col] = lt;
     }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d0 = 16 * db + 4 * g;
-      if (d0 < D) {
-        float* dst = a.part_o + (base + col) * D + d0;
-        *reinterpret_cast<f32x4*>(dst) = st.o[db][cb];
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        const int d0 = 32 * db + 8 * aa + 4 * h;
+        if (d0 < D) {
+          float* dst = a.part_o + (base + col) * D + d0;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{st.o[db][cb][4 * aa], st.o[db][cb][4 * aa + 1],
+                                                 st.o[db][cb][4 * aa + 2], st.o[db][cb][4 * aa + 3]};
+        }
       }
-    }
   }
 }
 
@@ -263,6 +432,9 @@ hipError_t launch_mfma(const EncodeParams& p, hipStream_t s) {
     FLAREPP_ENC(2)
     FLAREPP_ENC(4)
     FLAREPP_ENC(8)
+#if FLAREPP_ENC_NC == 1
+    FLAREPP_ENC(16)
+#endif
     default:
       return hipErrorInvalidValue;
   }
@@ -291,15 +463,15 @@ hipError_t launch_mfma_d(int D, const EncodeParams& p, hipStream_t s) {
 }  // namespace
 
 int encode_waves(int M) {
-  const int w = (M + 16 * kNC - 1) / (16 * kNC);
-  return w <= 1 ? 1 : w <= 2 ? 2 : w <= 4 ? 4 : 8;
+  const int w = (M + 32 * kNC - 1) / (32 * kNC);
+  return w <= 1 ? 1 : w <= 2 ? 2 : w <= 4 ? 4 : w <= 8 ? 8 : 16;
 }
 
 int latent_pad(int M, int dtype) {
   // fp32 path: one thread per latent row in blocks of 64; matrix-core path:
   // 64 latents per wave and a power-of-two wave count.
   if (dtype == kF32) return ((M + 63) / 64) * 64;
-  return encode_waves(M) * 16 * kNC;
+  return encode_waves(M) * 32 * kNC;
 }
 
 hipError_t launch_encode(int dtype, int D, const EncodeParams& p, hipStream_t s) {

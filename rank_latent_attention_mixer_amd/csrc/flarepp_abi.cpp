@@ -18,7 +18,6 @@ using namespace flarepp;
 
 constexpr int kEncTile = 64;        // token tile of the encoder (chunk granularity)
 constexpr int kEncTargetWgs = 512;  // encoder workgroups aimed for (2 per CU)
-constexpr int kDecTokTile = 512;    // tokens per decoder workgroup iteration
 constexpr int kDecTargetWgs = 1024;
 constexpr size_t kAlign = 256;
 
@@ -62,7 +61,7 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   if (chunk_tokens < 0 || (chunk_tokens % kEncTile) != 0) return FLAREPP_ERR_INVALID_ARGUMENT;
   p->B = B; p->H = H; p->N = N; p->M = M; p->D = D; p->dtype = dtype;
   p->Mpad = latent_pad((int)M, dtype);
-  p->DV = D < 16 ? 16 : (int)D;
+  p->DV = D < 32 ? 32 : (int)D;
   const int64_t BH = B * H;
   const int64_t tiles = (N + kEncTile - 1) / kEncTile;
   if (chunk_tokens == 0) {
@@ -77,7 +76,7 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   if (!mul_ok(BH, nchunks, &wgs) || wgs > 0x7FFFFFFF) return FLAREPP_ERR_INVALID_ARGUMENT;
   p->chunk_tokens = chunk_tokens;
   p->nchunks = (int)nchunks;
-  const int64_t dtiles = (N + kDecTokTile - 1) / kDecTokTile;
+  const int64_t dtiles = (N + decode_tokens_per_tile((int)D) - 1) / decode_tokens_per_tile((int)D);
   int64_t w = (kDecTargetWgs + BH - 1) / BH;
   if (w > dtiles) w = dtiles;
   if (w < 1) w = 1;
@@ -206,7 +205,8 @@ hipError_t decode(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh
 
 int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, const void* q0,
                const void* q_fixed, const float* gate, const void* k0, const void* k,
-               const void* v, void* y, void* ws, size_t ws_bytes, void* stream) {
+               const void* v, void* y, void* ws, size_t ws_bytes, void* stream,
+               void* const* events) {
   if (!q0 || !q_fixed || !gate || !k0 || !k || !v || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
   Plan p;
   int st = make_plan(B, H, N, M, D, dtype, 0, &p);
@@ -224,10 +224,16 @@ int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   const float c = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
   const int64_t BH = B * H;
   const int64_t qh = (int64_t)p.Mpad * D;
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+  };
+  FLAREPP_TRY(mark(0));
   // 1. seeds as operand, 2. synthesis partials (closed-gate heads skipped)
   FLAREPP_TRY(prep_latents(p, ws, p.off_q0, q0, 0, (int)H, c, s));
+  FLAREPP_TRY(mark(1));
   FLAREPP_TRY(launch_encode(dtype, (int)D,
                             encode_params(p, ws, ws_at(ws, p.off_q0), 0, qh, k0, k0, gate), s));
+  FLAREPP_TRY(mark(2));
   // 3. q = q_fixed + sigma * q_dyn, per (b, h), as operand
   {
     CombineParams cp = combine_base(p, ws);
@@ -243,13 +249,16 @@ int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
     cp.out_kind = dtype == FLAREPP_F32 ? kOutNatural32 : kOutNatural;
     FLAREPP_TRY(launch_combine(cp, s));
   }
+  FLAREPP_TRY(mark(3));
   // 4. encode partials, 5. z as value operand, 6. decode
   FLAREPP_TRY(launch_encode(dtype, (int)D,
                             encode_params(p, ws, ws_at(ws, p.off_q), H * qh, qh, k, v, nullptr),
                             s));
+  FLAREPP_TRY(mark(4));
   FLAREPP_TRY(value_operand(p, ws, p.nchunks, nullptr, nullptr, s));
+  FLAREPP_TRY(mark(5));
   FLAREPP_TRY(decode(p, ws, ws_at(ws, p.off_q), H * qh, qh, k, y, s));
-  (void)BH;
+  FLAREPP_TRY(mark(6));
   return FLAREPP_OK;
 }
 
@@ -320,7 +329,23 @@ int flarepp_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int
                       size_t workspace_bytes, void* stream) {
   try {
     return mixer_impl(B, H, N, M, D, dtype, q0, q_fixed, gate, k0, k, v, y, workspace,
-                      workspace_bytes, stream);
+                      workspace_bytes, stream, nullptr);
+  } catch (...) {
+    return FLAREPP_ERR_HIP;
+  }
+}
+
+int flarepp_mixer_fwd_timed(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                            const void* q0, const void* q_fixed, const float* gate,
+                            const void* k0, const void* k, const void* v, void* y,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events) {
+  try {
+    if (events == nullptr) return FLAREPP_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < FLAREPP_TIMED_EVENTS; ++i)
+      if (events[i] == nullptr) return FLAREPP_ERR_INVALID_ARGUMENT;
+    return mixer_impl(B, H, N, M, D, dtype, q0, q_fixed, gate, k0, k, v, y, workspace,
+                      workspace_bytes, stream, events);
   } catch (...) {
     return FLAREPP_ERR_HIP;
   }

@@ -1,20 +1,23 @@
 // Device-side building blocks shared by the FLARE++ kernels (gfx950 only).
 //
-// Matrix-core tile used throughout: v_mfma_f32_16x16x32_{bf16,f16}.
-// For D[16x16] += A[16x32] * B[32x16], lane l of the 64-wide wave supplies
-//   A[l % 16][8*(l/16) .. 8*(l/16)+7]   (8 consecutive k of one row)
-//   B[8*(l/16) .. +7][l % 16]           (8 consecutive k of one column)
-// and receives D[4*(l/16) + i][l % 16], i = 0..3.
+// Matrix-core tile used throughout: v_mfma_f32_32x32x16_{bf16,f16}.
+// For D[32x32] += A[32x16] * B[16x32], lane l of the 64-wide wave (h = l/32)
+// supplies
+//   A[l % 32][8h .. 8h+7]     (8 consecutive k of one row)
+//   B[8h .. 8h+7][l % 32]     (8 consecutive k of one column)
+// and receives the 16 values D[8a + 4h + i][l % 32], v = 4a + i (a, i = 0..3).
+// (The 32x32 shape is used rather than 16x16x32 because it leaves the VALU
+// far more room to run the softmax exponentials alongside the matrix core.)
 //
 // Attention is evaluated "transposed": for query columns r (held in
 // registers) and keys j (streamed), the score tile is S^T[j][r] =
-// K[j] . Q[r], so each lane owns one query column and four keys.  Those four
-// fp32 scores of two 16-key blocks become, after exp and packing, exactly the
-// 8 k-values that lane must supply as the B operand of the P.V product
+// K[j] . Q[r], so each lane owns one query column and 16 keys.  Those 16
+// fp32 scores, after exp and packing, are exactly the k-values that lane
+// must supply as the B operand of the two K=16 steps of the P.V product
 // O^T[d][r] += V^T[d][j] P^T[j][r].  The price is that V must be supplied
 // transposed (rows d, k = keys) in the key order the score layout implies:
-// within a 32-key group, operand slot s = 8g + 4h + i holds key
-// j = 16h + 4g + i (g = lane group, h = which 16-key block, i = 0..3).
+// within a 32-key group, operand slot s = 16kk + 8h + 4a + i holds key
+// j = 16kk + 8a + 4h + i.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,8 +30,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
 
 // log2(e): scores are carried in the base-2 domain so that exp is one
 // v_exp_f32.  The caller folds scale * log2(e) into the latent operand.
@@ -42,11 +48,11 @@ template <typename T> struct Pack8;
 template <> struct Pack8<__bf16> { typedef bf16x8 type; typedef bf16x2 pair; };
 template <> struct Pack8<_Float16> { typedef f16x8 type; typedef f16x2 pair; };
 
-__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_16x16x32(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Sum of a packed pair plus an fp32 accumulator (v_dot2 with ones).
@@ -75,6 +81,17 @@ __device__ __forceinline__ void stg16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// 16 bytes per lane from global memory straight into LDS (no registers):
+// lane i's data lands at lds_base + 16*i, lds_base being wave-uniform.
+// The builtin exists only in the device pass; in the host pass of the
+// single-source compile its presence would drop the kernel's launch stub.
+__device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   0);
+#endif
+}
+
 // Convert 8 fp32 to a packed 8-element operand (round to nearest even).
 template <typename T>
 __device__ __forceinline__ typename Pack8<T>::type pack8(float a0, float a1, float a2, float a3,
@@ -87,8 +104,16 @@ __device__ __forceinline__ typename Pack8<T>::type pack8(float a0, float a1, flo
 
 // Operand slot of key j within a 32-key group (see header comment).
 __host__ __device__ __forceinline__ int key_slot(int j) {
-  const int h = j >> 4, g = (j >> 2) & 3, i = j & 3;
-  return 8 * g + 4 * h + i;
+  const int kk = j >> 4, a = (j >> 3) & 1, h = (j >> 2) & 1, i = j & 3;
+  return 16 * kk + 8 * h + 4 * a + i;
+}
+
+// Row of a 32-row value block that must hold output column d (0..31) so
+// that the lane half h = d/16 receives columns 16h .. 16h+15 in order:
+// accumulator row 8a + 4h + i is value v = 4a + i of lane half h.
+__host__ __device__ __forceinline__ int value_row(int d) {
+  const int h = d >> 4, a = (d >> 2) & 3, i = d & 3;
+  return 8 * a + 4 * h + i;
 }
 
 // Logistic gate in fp32; -inf -> 0, +inf -> 1.

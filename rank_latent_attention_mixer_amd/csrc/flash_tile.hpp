@@ -1,157 +1,180 @@
-// Wave-level online-softmax attention step on the gfx950 matrix cores.
+// Wave-level online-softmax attention on the gfx950 matrix cores.
 //
-// One wave owns NC blocks of 16 query columns r (the "register side": the
+// One wave owns NC blocks of 32 query columns r (the "register side": the
 // latents in the encoder, the tokens in the decoder) and consumes keys in
 // groups of 32 (the "streamed side").  For every column it keeps
-//   ref  - the running reference m (base-2 score units); held negated and
-//          replicated four times so that it can be the C operand of the
-//          score product, which then returns S' - m directly;
+//   ref  - a reference m (base-2 score units), held negated and replicated
+//          so that it is the C operand of the score product, which then
+//          returns S' - m with no VALU subtraction;
 //   lsum - this lane's share of sum_j 2^(S'_j - m);
 //   o    - O^T[d][r] = sum_j 2^(S'_j - m) V[j][d]  (fp32 accumulators).
 // Scores S' are already in base-2 units: the caller folds scale * log2(e)
 // into the latent operand, so p = v_exp_f32(S' - m).
 //
-// The reference moves lazily: a group whose per-lane probability sum stays
-// below 2^8 is accepted as is (every p <= 2^8, so nothing can overflow and
-// no row maximum is needed).  Otherwise, and for the very first group, the
-// wave takes a slow path that finds the exact column maximum of the group,
-// moves the reference up to it and rescales the accumulators.  The result
-// is the same normalised softmax as with an eager running maximum; only the
-// intermediate scaling differs.
+// The reference is set once, to the exact column maximum of the first key
+// group, and never moves: the normalised result sum_j p_j v_j / sum_j p_j
+// does not depend on m, and in floating point only overflow could go wrong
+// -- a later score exceeding the reference by more than the range of the
+// probability type (2^127 for bf16, 2^15 for fp16) or the fp32 sums.  Such
+// inputs are detected once per column at the end (a non-finite l or O) and
+// the caller recomputes that wave's columns with the exact two-pass method
+// (global maximum first, then the sums).  The steady state therefore has no
+// branch, no maximum and no rescale: per 32 x 32 score block it issues 16
+// v_exp_f32, 8 v_cvt_pk and 8 v_dot2 next to four matrix-core ops.
 //
 // Sources for the operation: FLARE.py README, "FLARE++" and "FLARE"
-// listings (scaled-dot-product attention); the chunked statistics
+// listings (scaled-dot-product attention); the per-chunk statistics
 // (m, l, O) follow issue #2024, "Multi-GPU context parallelism" (latent-sized
 // outputs plus log-sum-exp statistics per token shard).
 #pragma once
+
+#include <type_traits>
 
 #include "flarepp_device.hpp"
 
 namespace flarepp {
 
+// compile-time integer argument for generic lambdas
+template <int V>
+using IntC = std::integral_constant<int, V>;
+
 template <typename T, int D, int NC>
 struct FlashTile {
-  static constexpr int KD = (D + 31) / 32;      // K=32 slices of the score product
-  static constexpr int DV = D < 16 ? 16 : D;    // value rows, padded to a 16-row block
-  static constexpr int NDB = DV / 16;           // 16-row blocks of O^T
+  static constexpr int DK = D < 16 ? 16 : D;   // contraction length of the score product
+  static constexpr int KD = DK / 16;           // K=16 steps of the score product
+  static constexpr int DV = D < 32 ? 32 : D;   // value rows, padded to a 32-row block
+  static constexpr int NDB = DV / 32;          // 32-row blocks of O^T
   typedef typename Pack8<T>::type V8;
-  typedef typename Pack8<T>::pair V2;
 
   V8 q[NC][KD];
-  f32x4 o[NDB][NC];
-  f32x4 negm[NC];
+  f32x16 o[NDB][NC];
+  f32x16 negm[NC];
   float lsum[NC];
-  bool first;
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
-      negm[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 16; ++v) negm[cb][v] = 0.f;
       lsum[cb] = 0.f;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][cb][v] = 0.f;
     }
-    first = true;
   }
 
-  // p = 2^s for the 8 scores of a column, packed as the B operand of the
-  // P.V product; ts = this lane's sum of the packed (rounded) values.
-  __device__ __forceinline__ static void exp_pack(const f32x4 (&s)[2][NC], V8 (&p)[NC],
-                                                  float (&ts)[NC]) {
+  // Score product of one key group: s[cb] = K . Q[cb]^T - m[cb]
+  // (kop[kd]: A operand, key lane%32, d = 16kd + 8h ..).
+  __device__ __forceinline__ void scores(const V8 (&kop)[KD], f32x16 (&s)[NC]) const {
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
-      float e[8];
+      s[cb] = mfma_32x32x16(kop[0], q[cb][0], negm[cb]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(s[0][cb][i]);
-        e[4 + i] = __builtin_amdgcn_exp2f(s[1][cb][i]);
-      }
-      p[cb] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      float acc = 0.f;
-      acc = pair_sum(__builtin_shufflevector(p[cb], p[cb], 0, 1), acc);
-      acc = pair_sum(__builtin_shufflevector(p[cb], p[cb], 2, 3), acc);
-      acc = pair_sum(__builtin_shufflevector(p[cb], p[cb], 4, 5), acc);
-      acc = pair_sum(__builtin_shufflevector(p[cb], p[cb], 6, 7), acc);
-      ts[cb] = acc;
+      for (int kd = 1; kd < KD; ++kd) s[cb] = mfma_32x32x16(kop[kd], q[cb][kd], s[cb]);
     }
   }
 
-  // Consume one group of 32 keys.
-  //   kop[jb][kd] : A operand of the score product, keys 16*jb + (lane%16)
-  //   vop[db]     : A operand of the P.V product, value rows of block db in
-  //                 key-slot order (see flarepp_device.hpp)
-  //   kvalid      : number of valid keys in the group (1..32); the others
-  //                 get probability 0
-  //   g           : lane / 16
-  __device__ __forceinline__ void step(const V8 (&kop)[2][KD], const V8 (&vop)[NDB], int kvalid,
-                                       int g) {
-    f32x4 s[2][NC];
+  // Keys j >= kvalid of the group get probability 0.
+  __device__ __forceinline__ static void mask(f32x16 (&s)[NC], int kvalid, int h) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+    for (int v = 0; v < 16; ++v) {
+      const int j = 8 * (v >> 2) + 4 * h + (v & 3);
+      if (j >= kvalid) {
 #pragma unroll
-      for (int cb = 0; cb < NC; ++cb) {
-        s[jb][cb] = mfma_16x16x32(kop[jb][0], q[cb][0], negm[cb]);
-#pragma unroll
-        for (int kd = 1; kd < KD; ++kd) s[jb][cb] = mfma_16x16x32(kop[jb][kd], q[cb][kd], s[jb][cb]);
+        for (int cb = 0; cb < NC; ++cb) s[cb][v] = -__builtin_inff();
       }
     }
-    if (kvalid < 32) {
+  }
+
+  // Column maximum of a group's scores (the two lanes of a column combined).
+  __device__ __forceinline__ static void colmax(const f32x16 (&s)[NC], float (&mx)[NC]) {
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+    for (int cb = 0; cb < NC; ++cb) {
+      float m = s[cb][0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = 16 * jb + 4 * g + i;
-          if (j >= kvalid) {
-#pragma unroll
-            for (int cb = 0; cb < NC; ++cb) s[jb][cb][i] = -__builtin_inff();
-          }
-        }
+      for (int v = 1; v < 16; ++v) m = fmaxf(m, s[cb][v]);
+      mx[cb] = fmaxf(m, __shfl_xor(m, 32));
     }
-    V8 p[NC];
-    float ts[NC];
-    exp_pack(s, p, ts);
-    bool need = first;
+  }
+
+  // Moves the reference by delta (scores s computed against the old one).
+  __device__ __forceinline__ void set_reference(f32x16 (&s)[NC], const float (&delta)[NC]) {
 #pragma unroll
-    for (int cb = 0; cb < NC; ++cb) need = need || (ts[cb] > kTauSum);
-    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-      // slow path: move each column's reference to the group's maximum
+    for (int cb = 0; cb < NC; ++cb) {
+      negm[cb] -= delta[cb];
+      s[cb] -= delta[cb];
+    }
+  }
+
+  // p = 2^s packed as the B operands of the two K=16 steps of the P.V
+  // product, the rounded values summed into lsum, then O += V^T P^T.
+  //   vop[db][kk] : A operand of the P.V product, value rows of block db,
+  //                 key slots 16kk + 8h .. (see flarepp_device.hpp)
+  __device__ __forceinline__ void accumulate(const f32x16 (&s)[NC], const V8 (&vop)[NDB][2]) {
+    V8 p[NC][2];
 #pragma unroll
-      for (int cb = 0; cb < NC; ++cb) {
-        float mx = s[0][cb][0];
+    for (int cb = 0; cb < NC; ++cb) {
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+      for (int kk = 0; kk < 2; ++kk) {
+        float e[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[jb][cb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float delta = first ? mx : fmaxf(mx, 0.f);
-        if (!first) {
-          const float sc = __builtin_amdgcn_exp2f(-delta);
-          lsum[cb] *= sc;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) o[db][cb] *= sc;
-        }
-        negm[cb] -= delta;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) s[jb][cb] -= delta;
+        for (int t = 0; t < 8; ++t) e[t] = __builtin_amdgcn_exp2f(s[cb][8 * kk + t]);
+        p[cb][kk] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+        float acc = lsum[cb];
+        acc = pair_sum(__builtin_shufflevector(p[cb][kk], p[cb][kk], 0, 1), acc);
+        acc = pair_sum(__builtin_shufflevector(p[cb][kk], p[cb][kk], 2, 3), acc);
+        acc = pair_sum(__builtin_shufflevector(p[cb][kk], p[cb][kk], 4, 5), acc);
+        acc = pair_sum(__builtin_shufflevector(p[cb][kk], p[cb][kk], 6, 7), acc);
+        lsum[cb] = acc;
       }
-      exp_pack(s, p, ts);
-      first = false;
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int cb = 0; cb < NC; ++cb) o[db][cb] = mfma_16x16x32(vop[db], p[cb], o[db][cb]);
-#pragma unroll
-    for (int cb = 0; cb < NC; ++cb) lsum[cb] += ts[cb];
+      for (int cb = 0; cb < NC; ++cb) {
+        o[db][cb] = mfma_32x32x16(vop[db][0], p[cb][0], o[db][cb]);
+        o[db][cb] = mfma_32x32x16(vop[db][1], p[cb][1], o[db][cb]);
+      }
   }
 
-  // Full row sum of column cb (the four lanes sharing the column).
+  // First group of a sweep: scores were computed with m = 0; the reference
+  // becomes the group's exact column maximum.
+  template <bool MASKED>
+  __device__ __forceinline__ void first(f32x16 (&s)[NC], const V8 (&vop)[NDB][2], int kvalid,
+                                        int h) {
+    if constexpr (MASKED) mask(s, kvalid, h);
+    float mx[NC];
+    colmax(s, mx);
+    set_reference(s, mx);
+    accumulate(s, vop);
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void next(f32x16 (&s)[NC], const V8 (&vop)[NDB][2], int kvalid,
+                                       int h) {
+    if constexpr (MASKED) mask(s, kvalid, h);
+    accumulate(s, vop);
+  }
+
+  // True (wave-uniform) if any column of the wave ended with a non-finite
+  // sum or output, i.e. the fixed reference was exceeded beyond range.
+  __device__ __forceinline__ bool overflowed() const {
+    bool bad = false;
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      bad = bad || !__builtin_isfinite(lsum[cb]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bad = bad || !__builtin_isfinite(o[db][cb][v]);
+    }
+    return __builtin_amdgcn_ballot_w64(bad) != 0ull;
+  }
+
+  // Full row sum of column cb (the two lanes sharing the column).
   __device__ __forceinline__ float row_sum(int cb) const {
-    float t = lsum[cb];
-    t += __shfl_xor(t, 16);
-    t += __shfl_xor(t, 32);
-    return t;
+    return lsum[cb] + __shfl_xor(lsum[cb], 32);
   }
 };
 

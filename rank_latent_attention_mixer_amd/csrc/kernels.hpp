@@ -79,5 +79,6 @@ hipError_t launch_decode(int dtype, int D, const DecodeParams& p, hipStream_t s)
 int encode_waves(int M);                 // waves per encoder workgroup
 int latent_pad(int M, int dtype);        // Mpad
 int decode_lds_bytes(int M, int D, int dtype);
+int decode_tokens_per_tile(int D);       // tokens per decoder workgroup iteration
 
 }  // namespace flarepp
