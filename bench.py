@@ -8,6 +8,8 @@ Prints one JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--cpu-seconds S | --no-cpu-baseline]
+  python bench.py --copy-calibration-mib S   (plain device copy of S MiB, for
+                                              scaling the HBM byte counters)
 """
 
 from __future__ import annotations
@@ -29,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 KERNELS = ["prep_seeds", "encode_synthesis", "combine_query", "encode", "combine_value",
            "decode"]
-COUNTER_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_million_token.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_million_token_bf16.txt")
 
 
 def log(*a):
@@ -70,6 +72,41 @@ def source_digest() -> str:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def read_traffic(path, workload, kernel):
+    """HBM bytes per launch of `kernel` from a counter summary made of lines
+    'key value...'; None unless it was taken on the current kernel sources."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) >= 2 and not line.startswith("#"):
+                kv[f[0]] = f[1:]
+    if kv.get("source_digest", [None])[0] != source_digest():
+        return None
+    if kv.get("workload", [None])[0] != workload:
+        return None
+    v = kv.get(f"hbm_bytes_per_launch.{kernel}")
+    return int(float(v[0])) if v else None
+
+
+def copy_calibration(mib):
+    """Times nothing: issues 5 plain device-to-device copies of `mib` MiB so
+    that a counter run can relate FETCH_SIZE / WRITE_SIZE to known bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.rand(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "copies": 5}),
+          flush=True)
+    return 0
 
 
 def algorithmic_work(w, sig_open):
@@ -131,6 +168,7 @@ def main(argv=None):
     ap.add_argument("--workload", default="million_token_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0)
     a = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -138,6 +176,9 @@ def main(argv=None):
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}, WORLD_SIZE {world}); "
               "the mixer is built and measured on a single MI355X", file=sys.stderr)
         return 2
+
+    if a.copy_calibration_mib > 0:
+        return copy_calibration(a.copy_calibration_mib)
 
     import numpy as np
     import torch
@@ -203,13 +244,7 @@ def main(argv=None):
     f_launch, b_launch = work[dom]
     dur = per_kernel[dom] / 1e3
     achieved = f_launch / dur / 1e12
-    traffic = None
-    if os.path.exists(COUNTER_FILE):
-        with open(COUNTER_FILE) as fh:
-            cf = json.load(fh)
-        k = cf.get("kernels", {}).get(dom)
-        if k and cf.get("source_digest") == source_digest() and cf.get("workload") == w.name:
-            traffic = k["hbm_bytes_per_launch"]
+    traffic = read_traffic(TRAFFIC_FILE, w.name, dom)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": dom,
@@ -231,6 +266,7 @@ def main(argv=None):
         "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
         "roofline": roofline,
         "cpu_baseline": None,
+        "source_digest": source_digest(),
     }
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, w, a.cpu_seconds)
