@@ -22,10 +22,10 @@ namespace {
 #define FLAREPP_DEC_NC 1
 #endif
 constexpr int kNC = FLAREPP_DEC_NC;
-// waves per workgroup: 16 (four per SIMD) where the registers allow it
+// waves per workgroup: three per SIMD where the registers allow it
 template <int D>
 struct DecodeWaves {
-  static constexpr int value = 8;
+  static constexpr int value = D >= 64 ? 8 : 12;
 };
 
 template <int D>
@@ -111,23 +111,39 @@ decode_kernel(DecodeParams a) {
             *reinterpret_cast<const V8*>(zsb + vl[db] + G * VSTEP + kk * 16 * (int)sizeof(T));
   };
 
-  for (int64_t tile = part; tile < ntiles; tile += a.wg_per_bh) {
+  // token rows of one tile for this wave, as the register-side operand;
+  // rows past N read as zero (their outputs are never stored)
+  auto load_tokens = [&](int64_t tile, V8 (&dst)[kNC][KD]) {
     const int64_t nb = tile * kTokTile + wave * 32 * kNC;
-    if (nb >= a.N) continue;  // wave-uniform; no barrier below
-    Tile st;
-    st.reset();
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
       const int64_t n = nb + cb * 32 + r;
 #pragma unroll
       for (int kd = 0; kd < KD; ++kd) {
         const int d0 = 16 * kd + 8 * h;
-        if (d0 < D && n < a.N) st.q[cb][kd] = bitcast_u4<V8>(ldg16(kg + n * D + d0));
-        else st.q[cb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+        if (d0 < D && n < a.N) dst[cb][kd] = bitcast_u4<V8>(ldg16(kg + n * D + d0));
+        else dst[cb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
       }
     }
-    // latent groups of 32: group 0 sets the references, full groups run as
-    // a two-stage pipeline (two score buffers alternating), then a masked
+  };
+
+  // The workgroup walks tiles part, part + wg_per_bh, ...; the token rows
+  // of the next tile are fetched while the current one is computed.
+  V8 nxt[kNC][KD];
+  if (part < ntiles) load_tokens(part, nxt);
+  for (int64_t tile = part; tile < ntiles; tile += a.wg_per_bh) {
+    const int64_t nb = tile * kTokTile + wave * 32 * kNC;
+    Tile st;
+    st.reset();
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb)
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) st.q[cb][kd] = nxt[cb][kd];
+    if (tile + a.wg_per_bh < ntiles) load_tokens(tile + a.wg_per_bh, nxt);
+    if (nb >= a.N) continue;  // wave-uniform; no barrier below
+    // latent groups of 32: group 0, then full groups as a two-stage
+    // pipeline (the score product of group G+1 is issued before the
+    // softmax of group G, two score buffers alternating), then a masked
     // tail group
     f32x16 sa[kNC], sb[kNC];
     {
@@ -145,27 +161,36 @@ decode_kernel(DecodeParams a) {
         kop_at(1, kop);
         st.scores(kop, sa);
       }
-      for (int G = 1; G < nfull; G += 2) {
-        const bool more = G + 1 < nfull;
-        if (more) {
+      int G = 1;
+      for (; G + 2 < nfull; G += 2) {  // groups G and G+1, then G+2's scores
+        {
           V8 kop[KD];
           kop_at(G + 1, kop);
           st.scores(kop, sb);
-        }
-        {
           V8 vop[NDB][2];
           vop_at(G, vop);
           st.template next<false>(sa, vop, 32, h);
         }
-        if (!more) break;
-        if (G + 2 < nfull) {
-          V8 kop[KD];
-          kop_at(G + 2, kop);
-          st.scores(kop, sa);
-        }
+        V8 kop[KD];
+        kop_at(G + 2, kop);
+        st.scores(kop, sa);
         V8 vop[NDB][2];
         vop_at(G + 1, vop);
         st.template next<false>(sb, vop, 32, h);
+      }
+      if (G + 1 < nfull) {  // two full groups left
+        V8 kop[KD];
+        kop_at(G + 1, kop);
+        st.scores(kop, sb);
+        V8 vop[NDB][2];
+        vop_at(G, vop);
+        st.template next<false>(sa, vop, 32, h);
+        vop_at(G + 1, vop);
+        st.template next<false>(sb, vop, 32, h);
+      } else {  // one
+        V8 vop[NDB][2];
+        vop_at(G, vop);
+        st.template next<false>(sa, vop, 32, h);
       }
     }
     if (nfull > 0 && mtail > 0) {
@@ -176,58 +201,70 @@ decode_kernel(DecodeParams a) {
       vop_at(nfull, vop);
       st.template next<true>(sa, vop, mtail, h);
     }
-    // fixed references overflowed: exact two-pass recompute of this wave's
-    // tokens (true maxima over all latents first, then the sums)
-    if (st.overflowed()) {
-      const int ngrp = nfull + (mtail > 0 ? 1 : 0);
-      float mx[kNC];
-#pragma unroll
-      for (int cb = 0; cb < kNC; ++cb) mx[cb] = -__builtin_inff();
-      st.reset();
-      for (int G = 0; G < ngrp; ++G) {
-        V8 kop[KD];
-        kop_at(G, kop);
-        st.scores(kop, sa);
-        Tile::mask(sa, a.M - 32 * G, h);
-        float gm[kNC];
-        Tile::colmax(sa, gm);
-#pragma unroll
-        for (int cb = 0; cb < kNC; ++cb) mx[cb] = fmaxf(mx[cb], gm[cb]);
-      }
-      st.set_reference(sa, mx);
-      for (int G = 0; G < ngrp; ++G) {
-        V8 kop[KD];
-        kop_at(G, kop);
-        st.scores(kop, sa);
-        V8 vop[NDB][2];
-        vop_at(G, vop);
-        st.template next<true>(sa, vop, a.M - 32 * G, h);
-      }
-    }
     // y = O / l; lane (h, r) owns columns 32db + 16h .. +15 of token r
+    auto store = [&](const auto& t) {
 #pragma unroll
-    for (int cb = 0; cb < kNC; ++cb) {
-      const float inv = 1.0f / st.row_sum(cb);
-      const int64_t n = nb + cb * 32 + r;
-      if (n < a.N) {
+      for (int cb = 0; cb < kNC; ++cb) {
+        const float inv = 1.0f / t.row_sum(cb);
+        const int64_t n = nb + cb * 32 + r;
+        if (n < a.N) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d0 = 32 * db + 16 * h;
-          if (d0 < D) {
-            T out[16];
+          for (int db = 0; db < NDB; ++db) {
+            const int d0 = 32 * db + 16 * h;
+            if (d0 < D) {
+              T out[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) out[v] = (T)(st.o[db][cb][v] * inv);
-            T* dst = yg + n * D + d0;
-            if constexpr (D >= 16) {
-              *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
-              *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(&out[8]);
-            } else {
-              *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
+              for (int v = 0; v < 16; ++v) out[v] = (T)(t.o[db][cb][v] * inv);
+              T* dst = yg + n * D + d0;
+              if constexpr (D >= 16) {
+                *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
+                *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(&out[8]);
+              } else {
+                *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
+              }
             }
           }
         }
       }
+    };
+    if (!st.overflowed()) {
+      store(st);
+      continue;
     }
+    // sums out of range for the fixed reference: exact two-pass recompute
+    // of this wave's tokens (true maxima over all latents first, then the
+    // sums)
+    using Exact = FlashTile<T, D, kNC, true>;
+    Exact ex;
+    ex.reset();
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb)
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) ex.q[cb][kd] = st.q[cb][kd];
+    const int ngrp = nfull + (mtail > 0 ? 1 : 0);
+    float mx[kNC];
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb) mx[cb] = -__builtin_inff();
+    for (int G = 0; G < ngrp; ++G) {
+      V8 kop[KD];
+      kop_at(G, kop);
+      ex.scores(kop, sa);
+      Exact::mask(sa, a.M - 32 * G, h);
+      float gm[kNC];
+      Exact::colmax(sa, gm);
+#pragma unroll
+      for (int cb = 0; cb < kNC; ++cb) mx[cb] = fmaxf(mx[cb], gm[cb]);
+    }
+    ex.set_reference(sa, mx);
+    for (int G = 0; G < ngrp; ++G) {
+      V8 kop[KD];
+      kop_at(G, kop);
+      ex.scores(kop, sa);
+      V8 vop[NDB][2];
+      vop_at(G, vop);
+      ex.template next<true>(sa, vop, a.M - 32 * G, h);
+    }
+    store(ex);
   }
 }
 

@@ -268,83 +268,95 @@ __global__ __launch_bounds__(64 * NW) void encode_split_kernel(EncodeParams a) {
     }
   }
 
-  // The fixed references overflowed (scores far above the first group's
-  // maximum): recompute this wave's columns exactly, straight from HBM --
-  // first the true column maxima, then the sums, where nothing can exceed 1.
-  if (st.overflowed()) {
-    auto kop_g = [&](int G, V8 (&kop)[KD]) {
-      const int tok = min(32 * G + r, ntok - 1);
-#pragma unroll
-      for (int kd = 0; kd < KD; ++kd) {
-        const int d0 = 16 * kd + 8 * h;
-        if (d0 < D) kop[kd] = bitcast_u4<V8>(ldg16(kbase + (n0 + tok) * D + d0));
-        else kop[kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
-      }
-    };
-    auto vop_g = [&](int G, V8 (&vop)[NDB][2]) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + r;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          V8 x;
-#pragma unroll
-          for (int t8 = 0; t8 < 8; ++t8) {
-            const int tok = min(32 * G + 16 * kk + 8 * (t8 >> 2) + 4 * h + (t8 & 3), ntok - 1);
-            x[t8] = d < D ? vbase[(n0 + tok) * D + d] : (T)0.f;
-          }
-          vop[db][kk] = x;
-        }
-      }
-    };
-    const int ngrp = (ntok + 31) / 32;
-    float mx[kNC];
-#pragma unroll
-    for (int cb = 0; cb < kNC; ++cb) mx[cb] = -__builtin_inff();
-    st.reset();
-    for (int G = 0; G < ngrp; ++G) {
-      V8 kop[KD];
-      kop_g(G, kop);
-      st.scores(kop, sa);
-      Tile::mask(sa, ntok - 32 * G, h);
-      float gm[kNC];
-      Tile::colmax(sa, gm);
-#pragma unroll
-      for (int cb = 0; cb < kNC; ++cb) mx[cb] = fmaxf(mx[cb], gm[cb]);
-    }
-    st.set_reference(sa, mx);
-    for (int G = 0; G < ngrp; ++G) {
-      V8 kop[KD];
-      kop_g(G, kop);
-      st.scores(kop, sa);
-      V8 vop[NDB][2];
-      vop_g(G, vop);
-      st.template next<true>(sa, vop, ntok - 32 * G, h);
-    }
-  }
-
-  // partials of this chunk
+  // partials of this chunk: reference m, row sum l and O per latent column
   const int64_t base = ((int64_t)bh * a.nchunks + chunk) * a.Mpad;
+  auto write_partials = [&](const auto& t) {
 #pragma unroll
-  for (int cb = 0; cb < kNC; ++cb) {
-    const int col = wave * 32 * kNC + cb * 32 + r;
-    const float lt = st.row_sum(cb);
-    if (h == 0) {
-      a.part_m[base + col] = -st.negm[cb][0];
-      a.part_l[base + col] = lt;
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int aa = 0; aa < 4; ++aa) {
-        const int d0 = 32 * db + 8 * aa + 4 * h;
-        if (d0 < D) {
-          float* dst = a.part_o + (base + col) * D + d0;
-          *reinterpret_cast<f32x4*>(dst) = f32x4{st.o[db][cb][4 * aa], st.o[db][cb][4 * aa + 1],
-                                                 st.o[db][cb][4 * aa + 2], st.o[db][cb][4 * aa + 3]};
-        }
+    for (int cb = 0; cb < kNC; ++cb) {
+      const int col = wave * 32 * kNC + cb * 32 + r;
+      const float lt = t.row_sum(cb);
+      if (h == 0) {
+        a.part_m[base + col] = t.reference(cb);
+        a.part_l[base + col] = lt;
       }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa) {
+          const int d0 = 32 * db + 8 * aa + 4 * h;
+          if (d0 < D) {
+            float* dst = a.part_o + (base + col) * D + d0;
+            *reinterpret_cast<f32x4*>(dst) =
+                f32x4{t.o[db][cb][4 * aa], t.o[db][cb][4 * aa + 1], t.o[db][cb][4 * aa + 2],
+                      t.o[db][cb][4 * aa + 3]};
+          }
+        }
+    }
+  };
+
+  // Sums out of range for the fixed reference: recompute this wave's columns
+  // exactly, straight from HBM -- first the true column maxima, then the
+  // sums, where no probability exceeds 1 and the largest is 1.
+  if (!st.overflowed()) {
+    write_partials(st);
+    return;
   }
+  auto kop_g = [&](int G, V8 (&kop)[KD]) {
+    const int tok = min(32 * G + r, ntok - 1);
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) {
+      const int d0 = 16 * kd + 8 * h;
+      if (d0 < D) kop[kd] = bitcast_u4<V8>(ldg16(kbase + (n0 + tok) * D + d0));
+      else kop[kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+    }
+  };
+  auto vop_g = [&](int G, V8 (&vop)[NDB][2]) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 32 * db + r;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        V8 x;
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) {
+          const int tok = min(32 * G + 16 * kk + 8 * (t8 >> 2) + 4 * h + (t8 & 3), ntok - 1);
+          x[t8] = d < D ? vbase[(n0 + tok) * D + d] : (T)0.f;
+        }
+        vop[db][kk] = x;
+      }
+    }
+  };
+  using Exact = FlashTile<T, D, kNC, true>;
+  Exact ex;
+  ex.reset();
+#pragma unroll
+  for (int cb = 0; cb < kNC; ++cb)
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) ex.q[cb][kd] = st.q[cb][kd];
+  const int ngrp = (ntok + 31) / 32;
+  float mx[kNC];
+#pragma unroll
+  for (int cb = 0; cb < kNC; ++cb) mx[cb] = -__builtin_inff();
+  for (int G = 0; G < ngrp; ++G) {
+    V8 kop[KD];
+    kop_g(G, kop);
+    ex.scores(kop, sa);
+    Exact::mask(sa, ntok - 32 * G, h);
+    float gm[kNC];
+    Exact::colmax(sa, gm);
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb) mx[cb] = fmaxf(mx[cb], gm[cb]);
+  }
+  ex.set_reference(sa, mx);
+  for (int G = 0; G < ngrp; ++G) {
+    V8 kop[KD];
+    kop_g(G, kop);
+    ex.scores(kop, sa);
+    V8 vop[NDB][2];
+    vop_g(G, vop);
+    ex.template next<true>(sa, vop, ntok - 32 * G, h);
+  }
+  write_partials(ex);
 }
 
 // fp32 path: one thread per latent row, exact fp32 arithmetic (VALU FMAs),

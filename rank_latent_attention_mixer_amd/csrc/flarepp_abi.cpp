@@ -18,7 +18,7 @@ using namespace flarepp;
 
 constexpr int kEncTile = 64;        // token tile of the encoder (chunk granularity)
 constexpr int kEncTargetWgs = 512;  // encoder workgroups aimed for (2 per CU)
-constexpr int kDecTargetWgs = 1024;
+constexpr int kDecTargetWgs = 256;   // persistent decoder workgroups (one per CU)
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }

@@ -40,10 +40,6 @@ typedef short short8v __attribute__((ext_vector_type(8)));
 // v_exp_f32.  The caller folds scale * log2(e) into the latent operand.
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Lazy rescaling threshold: probabilities of a tile may reach 2^kTau
-// relative to the running reference before the reference is moved.
-constexpr float kTauSum = 256.0f;  // 2^8
-
 template <typename T> struct Pack8;
 template <> struct Pack8<__bf16> { typedef bf16x8 type; typedef bf16x2 pair; };
 template <> struct Pack8<_Float16> { typedef f16x8 type; typedef f16x2 pair; };
@@ -54,15 +50,13 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-
-// Sum of a packed pair plus an fp32 accumulator (v_dot2 with ones).
-__device__ __forceinline__ float pair_sum(bf16x2 p, float acc) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+// v_mfma_f32_16x16x32: lane l supplies A[l%16][8(l/16) ..+7] and
+// B[8(l/16) ..+7][l%16] and receives D[4(l/16) + i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ float pair_sum(f16x2 p, float acc) {
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-  return __builtin_amdgcn_fdot2(p, ones, acc, false);
+__device__ __forceinline__ f32x4 mfma_16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 template <typename V>

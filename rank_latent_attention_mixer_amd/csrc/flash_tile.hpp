@@ -1,26 +1,36 @@
-// Wave-level online-softmax attention on the gfx950 matrix cores.
+// Wave-level softmax attention on the gfx950 matrix cores.
 //
 // One wave owns NC blocks of 32 query columns r (the "register side": the
 // latents in the encoder, the tokens in the decoder) and consumes keys in
-// groups of 32 (the "streamed side").  For every column it keeps
-//   ref  - a reference m (base-2 score units), held negated and replicated
-//          so that it is the C operand of the score product, which then
-//          returns S' - m with no VALU subtraction;
-//   lsum - this lane's share of sum_j 2^(S'_j - m);
-//   o    - O^T[d][r] = sum_j 2^(S'_j - m) V[j][d]  (fp32 accumulators).
-// Scores S' are already in base-2 units: the caller folds scale * log2(e)
-// into the latent operand, so p = v_exp_f32(S' - m).
+// groups of 32 (the "streamed side").  Per column it accumulates
+//   l - sum_j 2^(S'_j - m)                    (fp32, on the matrix cores)
+//   o - O^T[d][r] = sum_j 2^(S'_j - m) V[j][d]  (fp32 accumulators)
+// for a reference m that never moves during a sweep.  Scores S' are already
+// in base-2 units: the caller folds scale * log2(e) into the latent operand,
+// so p = v_exp_f32(S' - m).
 //
-// The reference is set once, to the exact column maximum of the first key
-// group, and never moves: the normalised result sum_j p_j v_j / sum_j p_j
-// does not depend on m, and in floating point only overflow could go wrong
-// -- a later score exceeding the reference by more than the range of the
-// probability type (2^127 for bf16, 2^15 for fp16) or the fp32 sums.  Such
-// inputs are detected once per column at the end (a non-finite l or O) and
-// the caller recomputes that wave's columns with the exact two-pass method
-// (global maximum first, then the sums).  The steady state therefore has no
-// branch, no maximum and no rescale: per 32 x 32 score block it issues 16
-// v_exp_f32, 8 v_cvt_pk and 8 v_dot2 next to four matrix-core ops.
+// The normalised result sum_j p_j v_j / sum_j p_j does not depend on m; m
+// only has to keep p inside the range of the probability type.
+//   * bf16 probabilities share fp32's exponent range, so m = 0 is used and
+//     no maximum is ever taken (REF = false).
+//   * fp16 probabilities (at most 2^15.9) take m = the exact column maximum
+//     of the first key group, held negated and replicated as the C operand
+//     of the score product, which then returns S' - m with no VALU work
+//     (REF = true).
+// A column whose sums come out non-finite, or (m = 0) so small that
+// probabilities may have left the normal range, is recomputed by the caller
+// with the exact two-pass method (true maximum first, then the sums).  The
+// steady state therefore has no branch, no maximum and no rescale: per
+// 32 x 32 score block a lane issues 16 v_exp_f32 and 8 packing conversions
+// next to two score, two P.V and two row-sum matrix-core ops.
+//
+// Row sums: summing the packed probabilities with v_dot2 forms a serial
+// chain of 8 dependent VALU ops per block.  Instead each packed operand is
+// also fed to a 16x16x32 matrix-core op whose A operand is a fixed 0/1
+// pattern: in that op's B layout lane l holds k-group l/16 = 2(l/32) + r/16
+// of column l%16, so row 0 of the pattern (ones on k-groups 0 and 2) sums
+// the 16 key slots of columns 0..15 and row 1 (k-groups 1 and 3) those of
+// columns 16..31.  Result row i of column n sits in lane n, element i.
 //
 // Sources for the operation: FLARE.py README, "FLARE++" and "FLARE"
 // listings (scaled-dot-product attention); the per-chunk statistics
@@ -38,25 +48,47 @@ namespace flarepp {
 template <int V>
 using IntC = std::integral_constant<int, V>;
 
-template <typename T, int D, int NC>
+template <typename T> struct ProbTraits;
+template <> struct ProbTraits<__bf16> {
+  static constexpr bool kRef = false;
+  static constexpr unsigned kOnePair = 0x3F803F80u;  // two bf16 1.0
+};
+template <> struct ProbTraits<_Float16> {
+  static constexpr bool kRef = true;
+  static constexpr unsigned kOnePair = 0x3C003C00u;  // two fp16 1.0
+};
+
+// Smallest row sum accepted with m = 0: below it the largest probability of
+// the column may be near the bottom of the normal range.
+constexpr float kMinRowSum = 0x1p-80f;
+
+template <typename T, int D, int NC, bool REF = ProbTraits<T>::kRef>
 struct FlashTile {
   static constexpr int DK = D < 16 ? 16 : D;   // contraction length of the score product
   static constexpr int KD = DK / 16;           // K=16 steps of the score product
   static constexpr int DV = D < 32 ? 32 : D;   // value rows, padded to a 32-row block
   static constexpr int NDB = DV / 32;          // 32-row blocks of O^T
+  static constexpr bool kRef = REF;
   typedef typename Pack8<T>::type V8;
 
   V8 q[NC][KD];
   f32x16 o[NDB][NC];
-  f32x16 negm[NC];
-  float lsum[NC];
+  f32x16 negm[REF ? NC : 1];  // -m, replicated (REF only)
+  f32x4 lacc[NC];             // row sums, see header
+  V8 sum_op;                  // 0/1 pattern, A operand of the row-sum product
 
   __device__ __forceinline__ void reset() {
+    const int lane = __lane_id();
+    const bool on = lane == 0 || lane == 32 || lane == 17 || lane == 49;
+    const unsigned w = on ? ProbTraits<T>::kOnePair : 0u;
+    sum_op = bitcast_u4<V8>(u32x4{w, w, w, w});
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
+      if constexpr (REF) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) negm[cb][v] = 0.f;
-      lsum[cb] = 0.f;
+        for (int v = 0; v < 16; ++v) negm[cb][v] = 0.f;
+      }
+      lacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -69,7 +101,11 @@ struct FlashTile {
   __device__ __forceinline__ void scores(const V8 (&kop)[KD], f32x16 (&s)[NC]) const {
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
-      s[cb] = mfma_32x32x16(kop[0], q[cb][0], negm[cb]);
+      if constexpr (REF) {
+        s[cb] = mfma_32x32x16(kop[0], q[cb][0], negm[cb]);
+      } else {
+        s[cb] = mfma_32x32x16(kop[0], q[cb][0], f32x16{});
+      }
 #pragma unroll
       for (int kd = 1; kd < KD; ++kd) s[cb] = mfma_32x32x16(kop[kd], q[cb][kd], s[cb]);
     }
@@ -100,6 +136,7 @@ struct FlashTile {
 
   // Moves the reference by delta (scores s computed against the old one).
   __device__ __forceinline__ void set_reference(f32x16 (&s)[NC], const float (&delta)[NC]) {
+    static_assert(REF, "reference only kept with REF");
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
       negm[cb] -= delta[cb];
@@ -108,7 +145,7 @@ struct FlashTile {
   }
 
   // p = 2^s packed as the B operands of the two K=16 steps of the P.V
-  // product, the rounded values summed into lsum, then O += V^T P^T.
+  // product; O += V^T P^T and l += 1^T P^T on the matrix cores.
   //   vop[db][kk] : A operand of the P.V product, value rows of block db,
   //                 key slots 16kk + 8h .. (see flarepp_device.hpp)
   __device__ __forceinline__ void accumulate(const f32x16 (&s)[NC], const V8 (&vop)[NDB][2]) {
@@ -121,12 +158,6 @@ struct FlashTile {
 #pragma unroll
         for (int t = 0; t < 8; ++t) e[t] = __builtin_amdgcn_exp2f(s[cb][8 * kk + t]);
         p[cb][kk] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-        float acc = lsum[cb];
-        acc = pair_sum(__builtin_shufflevector(p[cb][kk], p[cb][kk], 0, 1), acc);
-        acc = pair_sum(__builtin_shufflevector(p[cb][kk], p[cb][kk], 2, 3), acc);
-        acc = pair_sum(__builtin_shufflevector(p[cb][kk], p[cb][kk], 4, 5), acc);
-        acc = pair_sum(__builtin_shufflevector(p[cb][kk], p[cb][kk], 6, 7), acc);
-        lsum[cb] = acc;
       }
     }
 #pragma unroll
@@ -136,17 +167,24 @@ struct FlashTile {
         o[db][cb] = mfma_32x32x16(vop[db][0], p[cb][0], o[db][cb]);
         o[db][cb] = mfma_32x32x16(vop[db][1], p[cb][1], o[db][cb]);
       }
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      lacc[cb] = mfma_16x16x32(sum_op, p[cb][0], lacc[cb]);
+      lacc[cb] = mfma_16x16x32(sum_op, p[cb][1], lacc[cb]);
+    }
   }
 
-  // First group of a sweep: scores were computed with m = 0; the reference
-  // becomes the group's exact column maximum.
+  // First group of a sweep.  REF: the scores were computed with m = 0 and
+  // the reference becomes the group's exact column maximum.
   template <bool MASKED>
   __device__ __forceinline__ void first(f32x16 (&s)[NC], const V8 (&vop)[NDB][2], int kvalid,
                                         int h) {
     if constexpr (MASKED) mask(s, kvalid, h);
-    float mx[NC];
-    colmax(s, mx);
-    set_reference(s, mx);
+    if constexpr (REF) {
+      float mx[NC];
+      colmax(s, mx);
+      set_reference(s, mx);
+    }
     accumulate(s, vop);
   }
 
@@ -157,24 +195,36 @@ struct FlashTile {
     accumulate(s, vop);
   }
 
-  // True (wave-uniform) if any column of the wave ended with a non-finite
-  // sum or output, i.e. the fixed reference was exceeded beyond range.
+  // Full row sum of this lane's column r = lane % 32 of block cb.
+  __device__ __forceinline__ float row_sum(int cb) const {
+    const int lane = __lane_id();
+    const float lo = __shfl(lacc[cb][0], lane & 15);  // columns 0..15
+    const float hi = __shfl(lacc[cb][1], lane & 15);  // columns 16..31
+    return (lane & 16) ? hi : lo;
+  }
+
+  // Reference m of column block cb (base-2 units).
+  __device__ __forceinline__ float reference(int cb) const {
+    if constexpr (REF) return -negm[cb][0];
+    else return 0.f;
+  }
+
+  // True (wave-uniform) if any column of the wave needs the exact two-pass
+  // recompute: a non-finite sum or output, or (m = 0) a row sum so small
+  // that its probabilities may have been flushed or lost precision.
   __device__ __forceinline__ bool overflowed() const {
     bool bad = false;
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
-      bad = bad || !__builtin_isfinite(lsum[cb]);
+      const float l = row_sum(cb);
+      bad = bad || !__builtin_isfinite(l);
+      if constexpr (!REF) bad = bad || !(l >= kMinRowSum);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) bad = bad || !__builtin_isfinite(o[db][cb][v]);
     }
     return __builtin_amdgcn_ballot_w64(bad) != 0ull;
-  }
-
-  // Full row sum of column cb (the two lanes sharing the column).
-  __device__ __forceinline__ float row_sum(int cb) const {
-    return lsum[cb] + __shfl_xor(lsum[cb], 32);
   }
 };
 
