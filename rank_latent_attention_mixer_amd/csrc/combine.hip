@@ -5,6 +5,9 @@
 //   m* = max_c m_c
 // is the log-sum-exp reduction of issue #2024, "Multi-GPU context
 // parallelism" (exact token-sharded encoder), applied across token chunks.
+// It is evaluated as pairwise merges of (m, l, O) states in a fixed order
+// (each of four lanes takes every fourth chunk, then a fixed butterfly), so
+// the result does not depend on timing.
 //
 // Query mode (after the synthesis): q = q_fixed + sigma(g_h) * merged, the
 // "Fixed reference and gate" update of issue #2024 "Changes from v1 to v2";
@@ -35,57 +38,115 @@ __device__ __forceinline__ void store_from_float(void* p, int64_t i, int dtype, 
   else reinterpret_cast<float*>(p)[i] = x;
 }
 
-__device__ __forceinline__ float merged_value(const CombineParams& a, int set, int m, int d) {
-  const int64_t base = (int64_t)set * a.nchunks * a.Mpad + m;
-  float mstar = -__builtin_inff();
-  for (int c = 0; c < a.nchunks; ++c) mstar = fmaxf(mstar, a.part_m[base + (int64_t)c * a.Mpad]);
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < a.nchunks; ++c) {
-    const int64_t i = base + (int64_t)c * a.Mpad;
-    const float w = exp2f(a.part_m[i] - mstar);
-    L = fmaf(w, a.part_l[i], L);
-    O = fmaf(w, a.part_o[i * a.D + d], O);
-  }
-  return O / L;
+// Running log-sum-exp state of one (latent, 4 columns) slot.
+struct Lse {
+  float m, l;
+  f32x4 o;
+};
+
+// a (+) b: both rescaled to the larger reference; an empty side (m = -inf)
+// contributes nothing.
+__device__ __forceinline__ Lse lse_merge(const Lse& a, const Lse& b) {
+  const float mn = fmaxf(a.m, b.m);
+  const float wa = a.m == -__builtin_inff() ? 0.f : exp2f(a.m - mn);
+  const float wb = b.m == -__builtin_inff() ? 0.f : exp2f(b.m - mn);
+  Lse r;
+  r.m = mn;
+  r.l = a.l * wa + b.l * wb;
+  r.o = a.o * wa + b.o * wb;
+  return r;
 }
 
-
+// One thread per (latent set, latent m, 4 output columns, chunk quarter):
+// each of the four lanes of a slot merges every fourth chunk, then the
+// lanes combine in a fixed butterfly and the first lane writes.
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
   const int set = blockIdx.y;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int width = a.out_kind == kOutValueT ? a.DV : a.D;
-  if (idx >= (int64_t)a.Mpad * width) return;
-  const int m = (int)(idx / width), d = (int)(idx - (int64_t)m * width);
+  const int W4 = (a.out_kind == kOutValueT ? a.DV : a.D) / 4;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int quarter = (int)(t & 3);
+  const int64_t slot = t >> 2;
+  const bool in_range = slot < (int64_t)a.Mpad * W4;  // all lanes stay for the shuffles
+  const int m = in_range ? (int)(slot / W4) : 0;
+  const int d0 = in_range ? 4 * (int)(slot - (int64_t)m * W4) : 0;
   const int h = set % a.H;
-  const bool live = (m < a.M) && (d < a.D);
+  const bool live = in_range && m < a.M && d0 < a.D;  // D is a multiple of 4
 
-  float val = 0.f;
+  float sg = 1.f;
+  bool use_parts = a.nchunks > 0;
   if (a.mode == kModeQuery) {
+    sg = (a.force_fixed || a.gate == nullptr) ? (a.force_fixed ? 0.f : 1.f) : gate_sigma(a.gate[h]);
+    use_parts = use_parts && sg != 0.f;
+  }
+
+  f32x4 merged = {0.f, 0.f, 0.f, 0.f};
+  if (use_parts) {  // uniform over the grid
+    Lse st{-__builtin_inff(), 0.f, {0.f, 0.f, 0.f, 0.f}};
     if (live) {
-      const int b = set / a.H;
-      const float fx = a.fixed ? load_as_float(a.fixed, b * a.fixed_b_stride +
-                                                            ((int64_t)h * a.M + m) * a.D + d,
-                                               a.fixed_dtype)
-                               : 0.f;
-      const float sg = (a.force_fixed || a.gate == nullptr) ? (a.force_fixed ? 0.f : 1.f)
-                                                            : gate_sigma(a.gate[h]);
-      val = (sg == 0.f || a.nchunks == 0) ? fx : fmaf(sg, merged_value(a, set, m, d), fx);
-      val *= a.cscale;
+      const int64_t base = (int64_t)set * a.nchunks * a.Mpad + m;
+#pragma unroll 4
+      for (int c = quarter; c < a.nchunks; c += 4) {
+        const int64_t i = base + (int64_t)c * a.Mpad;
+        Lse x;
+        x.m = a.part_m[i];
+        x.l = a.part_l[i];
+        x.o = *reinterpret_cast<const f32x4*>(a.part_o + i * a.D + d0);
+        st = lse_merge(st, x);
+      }
     }
-  } else {
-    if (live) {
-      val = a.nchunks == 0 ? a.z_in[((int64_t)set * a.M + m) * a.D + d]
-                           : merged_value(a, set, m, d);
-      if (a.z_out) a.z_out[((int64_t)set * a.M + m) * a.D + d] = val;
+#pragma unroll
+    for (int x = 1; x <= 2; x <<= 1) {
+      Lse o;
+      o.m = __shfl_xor(st.m, x);
+      o.l = __shfl_xor(st.l, x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o.o[e] = __shfl_xor(st.o[e], x);
+      st = lse_merge(st, o);
+    }
+    merged = st.o / st.l;
+  }
+  if (!in_range || quarter != 0) return;
+
+  float val[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    if (a.mode == kModeQuery) {
+      const int b = set / a.H;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fx =
+            a.fixed ? load_as_float(a.fixed, b * a.fixed_b_stride + ((int64_t)h * a.M + m) * a.D + d0 + e,
+                                    a.fixed_dtype)
+                    : 0.f;
+        val[e] = (use_parts ? fmaf(sg, merged[e], fx) : fx) * a.cscale;
+      }
+    } else {
+      const int64_t zi = ((int64_t)set * a.M + m) * a.D + d0;
+      if (a.nchunks == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = a.z_in[zi + e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = merged[e];
+      }
+      if (a.z_out) {  // caller memory: element stores, no alignment assumed
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a.z_out[zi + e] = val[e];
+      }
     }
   }
   if (a.out_kind == kOutValueT) {
-    const int row = (d & ~31) + value_row(d & 31);  // padded columns map to zero rows
     const int col = (m & ~31) + key_slot(m & 31);
-    store_from_float(a.out, ((int64_t)set * a.DV + row) * a.Mpad + col, a.out_dtype, val);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = d0 + e;
+      const int row = (d & ~31) + value_row(d & 31);  // padded columns map to zero rows
+      store_from_float(a.out, ((int64_t)set * a.DV + row) * a.Mpad + col, a.out_dtype, val[e]);
+    }
   } else {
-    store_from_float(a.out, ((int64_t)set * a.Mpad + m) * a.D + d,
-                     a.out_kind == kOutNatural32 ? (int)kF32 : a.out_dtype, val);
+    const int od = a.out_kind == kOutNatural32 ? (int)kF32 : a.out_dtype;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      store_from_float(a.out, ((int64_t)set * a.Mpad + m) * a.D + d0 + e, od, val[e]);
   }
 }
 
@@ -93,7 +154,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   const int width = p.out_kind == kOutValueT ? p.DV : p.D;
-  const int64_t n = (int64_t)p.Mpad * width;
+  const int64_t n = (int64_t)p.Mpad * (width / 4) * 4;  // (latent, 4 columns, chunk quarter)
   const dim3 grid((unsigned)((n + 255) / 256), (unsigned)p.nsets);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
   return hipGetLastError();
