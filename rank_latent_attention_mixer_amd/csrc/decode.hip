@@ -22,10 +22,13 @@ namespace {
 #define FLAREPP_DEC_NC 1
 #endif
 constexpr int kNC = FLAREPP_DEC_NC;
-// waves per workgroup: three per SIMD where the registers allow it
+// waves per workgroup (build-time knob for D <= 32)
+#ifndef FLAREPP_DEC_WAVES
+#define FLAREPP_DEC_WAVES 12
+#endif
 template <int D>
 struct DecodeWaves {
-  static constexpr int value = D >= 64 ? 8 : 12;
+  static constexpr int value = D >= 64 ? 8 : FLAREPP_DEC_WAVES;
 };
 
 template <int D>

@@ -96,6 +96,32 @@ __device__ __forceinline__ typename Pack8<T>::type pack8(float a0, float a1, flo
   return r;
 }
 
+// Eight probabilities packed as a matrix-core operand, rounded toward zero:
+// bf16 keeps the upper half of each fp32 (one v_perm_b32 per pair), fp16
+// uses the packed round-toward-zero conversion.  Only the spread of the
+// per-element rounding errors reaches the normalised result -- a common
+// factor cancels between numerator and row sum -- and that spread is one
+// unit in the last place for truncation as for round-to-nearest.
+template <typename T>
+__device__ __forceinline__ typename Pack8<T>::type pack_probs(const float (&e)[8]);
+template <>
+__device__ __forceinline__ bf16x8 pack_probs<__bf16>(const float (&e)[8]) {
+  u32x4 w;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    w[t] = __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, e[2 * t + 1]),
+                                 __builtin_bit_cast(unsigned, e[2 * t]), 0x07060302u);
+  return __builtin_bit_cast(bf16x8, w);
+}
+template <>
+__device__ __forceinline__ f16x8 pack_probs<_Float16>(const float (&e)[8]) {
+  u32x4 w;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    w[t] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(e[2 * t], e[2 * t + 1]));
+  return __builtin_bit_cast(f16x8, w);
+}
+
 // Operand slot of key j within a 32-key group (see header comment).
 __host__ __device__ __forceinline__ int key_slot(int j) {
   const int kk = j >> 4, a = (j >> 3) & 1, h = (j >> 2) & 1, i = j & 3;

@@ -21,8 +21,9 @@
 // probabilities may have left the normal range, is recomputed by the caller
 // with the exact two-pass method (true maximum first, then the sums).  The
 // steady state therefore has no branch, no maximum and no rescale: per
-// 32 x 32 score block a lane issues 16 v_exp_f32 and 8 packing conversions
-// next to two score, two P.V and two row-sum matrix-core ops.
+// 32 x 32 score block a lane issues 16 v_exp_f32 and 4 packing ops per 8
+// probabilities (v_perm_b32, see pack_probs) next to two score, two P.V and
+// two row-sum matrix-core ops.
 //
 // Row sums: summing the packed probabilities with v_dot2 forms a serial
 // chain of 8 dependent VALU ops per block.  Instead each packed operand is
@@ -47,6 +48,10 @@ namespace flarepp {
 // compile-time integer argument for generic lambdas
 template <int V>
 using IntC = std::integral_constant<int, V>;
+
+#ifndef FLAREPP_SCORE_PRIO
+#define FLAREPP_SCORE_PRIO 0
+#endif
 
 template <typename T> struct ProbTraits;
 template <> struct ProbTraits<__bf16> {
@@ -99,6 +104,9 @@ struct FlashTile {
   // Score product of one key group: s[cb] = K . Q[cb]^T - m[cb]
   // (kop[kd]: A operand, key lane%32, d = 16kd + 8h ..).
   __device__ __forceinline__ void scores(const V8 (&kop)[KD], f32x16 (&s)[NC]) const {
+#if FLAREPP_SCORE_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
       if constexpr (REF) {
@@ -109,6 +117,9 @@ struct FlashTile {
 #pragma unroll
       for (int kd = 1; kd < KD; ++kd) s[cb] = mfma_32x32x16(kop[kd], q[cb][kd], s[cb]);
     }
+#if FLAREPP_SCORE_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
   }
 
   // Keys j >= kvalid of the group get probability 0.
@@ -157,7 +168,7 @@ struct FlashTile {
         float e[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) e[t] = __builtin_amdgcn_exp2f(s[cb][8 * kk + t]);
-        p[cb][kk] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+        p[cb][kk] = pack_probs<T>(e);
       }
     }
 #pragma unroll
