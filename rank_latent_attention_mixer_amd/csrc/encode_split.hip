@@ -10,7 +10,7 @@
 // are staged in LDS in their natural [token][d] layout.  The P.V product contracts over tokens, so
 // its matrix-core operand needs V with tokens along k: it is read with the
 // transposing LDS load (ds_read_b64_tr_b16) instead of being transposed in
-// flight.  Tiles of 64 tokens rotate over three LDS buffers; the loads of
+// flight.  Tiles of kTJ tokens rotate over three LDS buffers; the loads of
 // tile t+1 are in flight while tile t is computed.
 #include "flash_tile.hpp"
 #include "kernels.hpp"
@@ -26,8 +26,11 @@ namespace {
 #endif
 constexpr int kNC = FLAREPP_ENC_NC;
 constexpr int kMaxWaves = 16 / kNC;   // waves per workgroup for M = 512
-constexpr int kTJ = 64;       // tokens per LDS tile
-constexpr int kGPT = kTJ / 32;  // 32-key groups per tile
+#ifndef FLAREPP_ENC_TILE
+#define FLAREPP_ENC_TILE 128
+#endif
+constexpr int kTJ = FLAREPP_ENC_TILE;  // tokens per LDS tile
+constexpr int kGPT = kTJ / 32;         // 32-key groups per tile
 // LDS tiles rotate over three buffers: with the score product running one
 // group ahead, a wave may still read tile t-1 while others fill tile t+1.
 constexpr int kNBUF = 3;
@@ -174,54 +177,66 @@ __global__ __launch_bounds__(64 * NW) void encode_split_kernel(EncodeParams a) {
       }
   };
 
-  // Key groups of 32 tokens, two per 64-token tile.  Tile 0 runs plainly
-  // (its first group sets the references).  Full tiles 1 .. nft-1 run as a
-  // two-stage pipeline -- the score product of the next group is issued
-  // before the softmax of the current one, two score buffers alternating --
-  // with the buffer rotation unrolled so every LDS address is a lane base
-  // plus an immediate.  A partial last tile follows.
+  // Key groups of 32 tokens, kGPT per tile.  Tile 0 runs plainly (its first
+  // group sets the references).  Full tiles 1 .. nft-1 run as a two-stage
+  // pipeline -- the score product of the next group is issued before the
+  // softmax of the current one, two score buffers alternating (group g of a
+  // tile in sa for even g, sb for odd g) -- with the buffer rotation unrolled
+  // so every LDS address is a lane base plus an immediate.  A partial last
+  // tile follows.
+  static_assert(kGPT % 2 == 0, "tiles hold an even number of key groups");
   const int nft = ntok / kTJ;  // full tiles
   f32x16 sa[kNC], sb[kNC];
+  auto sbuf = [&](auto gc) -> f32x16(&)[kNC] {
+    if constexpr (decltype(gc)::value % 2 == 0) return sa;
+    else return sb;
+  };
   issue_loads(lds0, 0);
   enter_tile(IntC<0>{}, 0);
-  {
-    V8 kop[KD];
-    kop_at(lds0, 0, kop);
-    st.scores(kop, sa);
-    V8 vop[NDB][2];
-    vop_at(lds0, 0, vop);
-    if (ntok >= 32) st.template first<false>(sa, vop, 32, h);
-    else st.template first<true>(sa, vop, ntok, h);
-  }
-  if (ntok > 32) {
-    V8 kop[KD];
-    kop_at(lds0, 1, kop);
-    st.scores(kop, sa);
-    V8 vop[NDB][2];
-    vop_at(lds0, 1, vop);
-    if (ntok >= 64) st.template next<false>(sa, vop, 32, h);
-    else st.template next<true>(sa, vop, ntok - 32, h);
-  }
+  static_for<kGPT>([&](auto gc) {
+    constexpr int g = decltype(gc)::value;
+    if (32 * g < ntok) {
+      const int kvalid = min(32, ntok - 32 * g);
+      V8 kop[KD];
+      kop_at(lds0, g, kop);
+      st.scores(kop, sa);
+      V8 vop[NDB][2];
+      vop_at(lds0, g, vop);
+      if constexpr (g == 0) {
+        if (kvalid == 32) st.template first<false>(sa, vop, 32, h);
+        else st.template first<true>(sa, vop, kvalid, h);
+      } else {
+        if (kvalid == 32) st.template next<false>(sa, vop, 32, h);
+        else st.template next<true>(sa, vop, kvalid, h);
+      }
+    }
+  });
+  // groups 0 .. kGPT-2 of a full tile in `cur`: on entry sbuf(0) holds the
+  // scores of group 0, on exit sbuf(kGPT-1) those of the last group
+  auto tile_groups = [&](const unsigned char* cur) {
+    static_for<kGPT - 1>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      V8 kop[KD];
+      kop_at(cur, g + 1, kop);
+      st.scores(kop, sbuf(IntC<g + 1>{}));
+      V8 vop[NDB][2];
+      vop_at(cur, g, vop);
+      st.template next<false>(sbuf(gc), vop, 32, h);
+    });
+  };
   // tile t in buffer B whose successor t+1 is also full; on entry sa holds
   // the scores of tile t's first group, on exit those of tile t+1's
   auto tile_body = [&](auto bc, int t) {
     constexpr int B = decltype(bc)::value, BN = (B + 1) % kNBUF;
     const unsigned char* cur = buf_c(bc);
-    {
-      V8 kop[KD];
-      kop_at(cur, 1, kop);
-      st.scores(kop, sb);
-      V8 vop[NDB][2];
-      vop_at(cur, 0, vop);
-      st.template next<false>(sa, vop, 32, h);
-    }
+    tile_groups(cur);
     enter_tile(IntC<BN>{}, t + 1);
     V8 kop[KD];
     kop_at(buf_c(IntC<BN>{}), 0, kop);
     st.scores(kop, sa);
     V8 vop[NDB][2];
-    vop_at(cur, 1, vop);
-    st.template next<false>(sb, vop, 32, h);
+    vop_at(cur, kGPT - 1, vop);
+    st.template next<false>(sbuf(IntC<kGPT - 1>{}), vop, 32, h);
   };
   if (nft > 1) {
     enter_tile(IntC<1>{}, 1);
@@ -241,16 +256,12 @@ __global__ __launch_bounds__(64 * NW) void encode_split_kernel(EncodeParams a) {
     }
     // last full tile, t = nft - 1
     const unsigned char* cur = buf_rt(t % kNBUF);
-    V8 kop[KD];
-    kop_at(cur, 1, kop);
-    st.scores(kop, sb);
+    tile_groups(cur);
     V8 vop[NDB][2];
-    vop_at(cur, 0, vop);
-    st.template next<false>(sa, vop, 32, h);
-    vop_at(cur, 1, vop);
-    st.template next<false>(sb, vop, 32, h);
+    vop_at(cur, kGPT - 1, vop);
+    st.template next<false>(sbuf(IntC<kGPT - 1>{}), vop, 32, h);
   }
-  // the partial last tile (1..63 tokens) after full ones
+  // the partial last tile (1 .. kTJ-1 tokens) after full ones
   const int rem = ntok - nft * kTJ;
   if (nft > 0 && rem > 0) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -473,6 +484,8 @@ hipError_t launch_mfma_d(int D, const EncodeParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int encode_tile_tokens() { return kTJ; }
 
 int encode_waves(int M) {
   const int w = (M + 32 * kNC - 1) / (32 * kNC);

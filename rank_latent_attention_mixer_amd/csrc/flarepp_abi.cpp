@@ -16,7 +16,7 @@ namespace {
 
 using namespace flarepp;
 
-constexpr int kEncTile = 64;        // token tile of the encoder (chunk granularity)
+constexpr int kEncTile = 64;        // granularity of caller-chosen encoder chunks
 constexpr int kEncTargetWgs = 512;  // encoder workgroups aimed for (2 per CU)
 constexpr int kDecTargetWgs = 256;   // persistent decoder workgroups (one per CU)
 constexpr size_t kAlign = 256;
@@ -63,13 +63,15 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   p->Mpad = latent_pad((int)M, dtype);
   p->DV = D < 32 ? 32 : (int)D;
   const int64_t BH = B * H;
-  const int64_t tiles = (N + kEncTile - 1) / kEncTile;
   if (chunk_tokens == 0) {
+    // automatic chunks: whole encoder tiles, about kEncTargetWgs workgroups
+    const int64_t unit = dtype == FLAREPP_F32 ? kEncTile : encode_tile_tokens();
+    const int64_t tiles = (N + unit - 1) / unit;
     int64_t c = (kEncTargetWgs + BH - 1) / BH;
     if (c < 1) c = 1;
     if (c > tiles) c = tiles;
     const int64_t chunk_tiles = (tiles + c - 1) / c;
-    chunk_tokens = chunk_tiles * kEncTile;
+    chunk_tokens = chunk_tiles * unit;
   }
   const int64_t nchunks = (N + chunk_tokens - 1) / chunk_tokens;
   int64_t wgs;

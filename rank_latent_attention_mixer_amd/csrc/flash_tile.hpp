@@ -40,6 +40,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "flarepp_device.hpp"
 
@@ -48,6 +49,16 @@ namespace flarepp {
 // compile-time integer argument for generic lambdas
 template <int V>
 using IntC = std::integral_constant<int, V>;
+
+// f(IntC<0>{}), f(IntC<1>{}), ..., f(IntC<N-1>{})
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(IntC<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 #ifndef FLAREPP_SCORE_PRIO
 #define FLAREPP_SCORE_PRIO 0

@@ -77,6 +77,7 @@ hipError_t launch_decode(int dtype, int D, const DecodeParams& p, hipStream_t s)
 
 // Launch-shape helpers shared with the workspace sizing.
 int encode_waves(int M);                 // waves per encoder workgroup
+int encode_tile_tokens();                // tokens per encoder LDS tile
 int latent_pad(int M, int dtype);        // Mpad
 int decode_lds_bytes(int M, int D, int dtype);
 int decode_tokens_per_tile(int D);       // tokens per decoder workgroup iteration
