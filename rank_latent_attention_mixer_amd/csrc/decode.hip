@@ -114,36 +114,39 @@ decode_kernel(DecodeParams a) {
             *reinterpret_cast<const V8*>(zsb + vl[db] + G * VSTEP + kk * 16 * (int)sizeof(T));
   };
 
-  // token rows of one tile for this wave, as the register-side operand;
-  // rows past N read as zero (their outputs are never stored)
+  // token rows of one tile for this wave, as the register-side operand.
+  // Rows past N re-read row N-1 (their outputs are never stored; every token
+  // column is independent), so the loads carry no condition and the
+  // compiler can wait for exactly the loads a tile needs.
   auto load_tokens = [&](int64_t tile, V8 (&dst)[kNC][KD]) {
     const int64_t nb = tile * kTokTile + wave * 32 * kNC;
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
-      const int64_t n = nb + cb * 32 + r;
+      const int64_t n = min(nb + cb * 32 + r, a.N - 1);
 #pragma unroll
       for (int kd = 0; kd < KD; ++kd) {
         const int d0 = 16 * kd + 8 * h;
-        if (d0 < D && n < a.N) dst[cb][kd] = bitcast_u4<V8>(ldg16(kg + n * D + d0));
-        else dst[cb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+        if constexpr (D >= 16) {
+          dst[cb][kd] = bitcast_u4<V8>(ldg16(kg + n * D + d0));
+        } else {  // D = 8: the upper half of the K=16 step is zero padding
+          if (d0 < D) dst[cb][kd] = bitcast_u4<V8>(ldg16(kg + n * D + d0));
+          else dst[cb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+        }
       }
     }
   };
 
-  // The workgroup walks tiles part, part + wg_per_bh, ...; the token rows
-  // of the next tile are fetched while the current one is computed.
-  V8 nxt[kNC][KD];
-  if (part < ntiles) load_tokens(part, nxt);
-  for (int64_t tile = part; tile < ntiles; tile += a.wg_per_bh) {
+  // One tile: the wave's 32 * kNC token rows arrive as qop (register
+  // operand); sweep all latents and store y.
+  auto process_tile = [&](int64_t tile, const V8 (&qop)[kNC][KD]) {
     const int64_t nb = tile * kTokTile + wave * 32 * kNC;
+    if (nb >= a.N) return;  // wave-uniform; no barrier below
     Tile st;
     st.reset();
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb)
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd) st.q[cb][kd] = nxt[cb][kd];
-    if (tile + a.wg_per_bh < ntiles) load_tokens(tile + a.wg_per_bh, nxt);
-    if (nb >= a.N) continue;  // wave-uniform; no barrier below
+      for (int kd = 0; kd < KD; ++kd) st.q[cb][kd] = qop[cb][kd];
     // latent groups of 32: group 0, then full groups as a two-stage
     // pipeline (the score product of group G+1 is issued before the
     // softmax of group G, two score buffers alternating), then a masked
@@ -232,7 +235,7 @@ decode_kernel(DecodeParams a) {
     };
     if (!st.overflowed()) {
       store(st);
-      continue;
+      return;
     }
     // sums out of range for the fixed reference: exact two-pass recompute
     // of this wave's tokens (true maxima over all latents first, then the
@@ -268,6 +271,26 @@ decode_kernel(DecodeParams a) {
       ex.template next<true>(sa, vop, a.M - 32 * G, h);
     }
     store(ex);
+  };
+
+  // The workgroup walks tiles part, part + wg_per_bh, ...; the token rows of
+  // the next tile are fetched into the other of two register sets while the
+  // current tile is computed (the loop is unrolled by two so the sets never
+  // need copying).
+  V8 qa[kNC][KD], qb[kNC][KD];
+  int64_t tile = part;
+  load_tokens(tile, qa);
+  while (tile < ntiles) {
+    // issued even past the last tile (rows clamp to N-1, results unused):
+    // no branch, so the waits before each tile count exactly its own loads
+    const int64_t t1 = tile + a.wg_per_bh;
+    load_tokens(t1, qb);
+    process_tile(tile, qa);
+    if (t1 >= ntiles) break;
+    const int64_t t2 = t1 + a.wg_per_bh;
+    load_tokens(t2, qa);
+    process_tile(t1, qb);
+    tile = t2;
   }
 }
 
