@@ -96,12 +96,15 @@ __device__ __forceinline__ typename Pack8<T>::type pack8(float a0, float a1, flo
   return r;
 }
 
-// Eight probabilities packed as a matrix-core operand, rounded toward zero:
-// bf16 keeps the upper half of each fp32 (one v_perm_b32 per pair), fp16
-// uses the packed round-toward-zero conversion.  Only the spread of the
-// per-element rounding errors reaches the normalised result -- a common
-// factor cancels between numerator and row sum -- and that spread is one
-// unit in the last place for truncation as for round-to-nearest.
+// Eight probabilities packed as a matrix-core operand.  bf16 keeps the upper
+// half of each fp32 (truncation, one v_perm_b32 per pair): only the spread
+// of the per-element rounding errors reaches the normalised result -- a
+// common factor cancels between numerator and row sum -- and that spread is
+// one unit in the last place for truncation as for round-to-nearest; an
+// infinite probability stays infinite.  fp16 rounds to nearest even
+// (v_cvt_pk_f16_f32), so a probability beyond the fp16 range becomes
+// infinite and the sweep's range check sees it (a saturating conversion
+// would hide it).
 template <typename T>
 __device__ __forceinline__ typename Pack8<T>::type pack_probs(const float (&e)[8]);
 template <>
@@ -115,11 +118,7 @@ __device__ __forceinline__ bf16x8 pack_probs<__bf16>(const float (&e)[8]) {
 }
 template <>
 __device__ __forceinline__ f16x8 pack_probs<_Float16>(const float (&e)[8]) {
-  u32x4 w;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    w[t] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(e[2 * t], e[2 * t + 1]));
-  return __builtin_bit_cast(f16x8, w);
+  return pack8<_Float16>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
 }
 
 // Operand slot of key j within a 32-key group (see header comment).

@@ -206,3 +206,74 @@ def test_deterministic(fp):
           for _ in range(3)]
     torch.cuda.synchronize()
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+
+
+# ---------------------------------------------------------------------------
+# The exact two-pass recompute.  The kernels sum 2^(S' - m) against a fixed
+# reference m (m = 0 for bf16 probabilities, the first key group's maximum
+# for fp16) and recompute a column exactly when its sums leave their range.
+# These inputs force that path: every score carries a large component that
+# is constant over the softmax axis (it cancels, so the exact result stays
+# well conditioned in bf16), or later keys exceed the first group's maximum
+# by more than the fp16 range.
+# ---------------------------------------------------------------------------
+
+FALLBACK = [
+    ("bf16", "shift", 70.0),   # sums overflow: every 2^S' is beyond fp32
+    ("bf16", "shift", -60.0),  # sums below the accepted range (2^-80)
+    ("fp16", "ramp", 20.0),    # keys after the first group exceed it by > 2^15.9
+]
+
+
+def _fallback_inputs(dtype, kind, amount, decoder, B=1, H=2, N=3000, M=80, D=32, seed=21):
+    from flarepp_workloads import round_to_dtype
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((H, M, D)).astype(np.float32)
+    k = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    v = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    if kind == "shift":
+        k[..., 0] = 8.0
+        q[..., 0] = amount
+    elif decoder:  # latents after the first group score higher
+        k[..., 0] = 4.0
+        q[:, :, 0] = np.where(np.arange(M) >= 32, amount, 0.0)
+    else:          # tokens after the first group score higher
+        k[..., 0] = np.where(np.arange(N) >= 32, 4.0, 0.0)
+        q[..., 0] = amount
+    return [round_to_dtype(a, dtype) for a in (q, k, v)]
+
+
+@pytest.mark.parametrize("dtype,kind,amount", FALLBACK)
+def test_encode_exact_recompute(fp, dtype, kind, amount):
+    q, k, v = _fallback_inputs(dtype, kind, amount, decoder=False)
+    s = 1.0 / math.sqrt(q.shape[-1])
+    dev = [torch.from_numpy(a).to(TDT[dtype]).cuda() for a in (q, k, v)]
+    note(f"[encode recompute] {dtype} {kind} {amount}")
+    z = fp.flare_encode_fwd(dev[0], dev[1], dev[2], s)
+    torch.cuda.synchronize()
+    ref = oracle.encode_ref(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), s)
+    z = z.cpu().numpy()
+    assert np.all(np.isfinite(z))
+    err = rel_err(z, ref)
+    note(f"[encode recompute] {dtype} {kind} {amount} rel err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,kind,amount", FALLBACK)
+def test_decode_exact_recompute(fp, dtype, kind, amount):
+    q, k, _ = _fallback_inputs(dtype, kind, amount, decoder=True)
+    B, H, N, D = k.shape
+    M = q.shape[1]
+    rng = np.random.Generator(np.random.PCG64(5))
+    z = rng.standard_normal((B, H, M, D)).astype(np.float32)
+    s = 1.0 / math.sqrt(D)
+    note(f"[decode recompute] {dtype} {kind} {amount}")
+    y = fp.flare_decode_fwd(torch.from_numpy(q).to(TDT[dtype]).cuda(), torch.from_numpy(z).cuda(),
+                            torch.from_numpy(k).to(TDT[dtype]).cuda(), s)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+    ref = oracle.decode_ref(q.astype(np.float64), z.astype(np.float64), k.astype(np.float64), s)
+    assert np.all(np.isfinite(y))
+    err = rel_err(y, ref)
+    note(f"[decode recompute] {dtype} {kind} {amount} rel err {err:.3e}")
+    assert err <= TOL[dtype]
