@@ -119,6 +119,10 @@ EDGE = [
     (2, 1, 129, 70, 16, "fp32"),
     (1, 1, 1000, 512, 64, "fp32"),
     (1, 2, 65, 33, 64, "fp32"),
+    (1, 2, 385, 512, 32, "bf16"),    # one token past a decoder tile, maximum M
+    (1, 1, 257, 96, 16, "bf16"),     # two encoder tiles plus one token
+    (3, 1, 128, 32, 32, "fp16"),     # exactly one encoder tile
+    (1, 1, 2000, 512, 64, "bf16"),   # wide heads at maximum M
 ]
 
 
