@@ -60,10 +60,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-#ifndef FLAREPP_SCORE_PRIO
-#define FLAREPP_SCORE_PRIO 0
-#endif
-
 template <typename T> struct ProbTraits;
 template <> struct ProbTraits<__bf16> {
   static constexpr bool kRef = false;
@@ -115,9 +111,6 @@ struct FlashTile {
   // Score product of one key group: s[cb] = K . Q[cb]^T - m[cb]
   // (kop[kd]: A operand, key lane%32, d = 16kd + 8h ..).
   __device__ __forceinline__ void scores(const V8 (&kop)[KD], f32x16 (&s)[NC]) const {
-#if FLAREPP_SCORE_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
       if constexpr (REF) {
@@ -128,9 +121,6 @@ struct FlashTile {
 #pragma unroll
       for (int kd = 1; kd < KD; ++kd) s[cb] = mfma_32x32x16(kop[kd], q[cb][kd], s[cb]);
     }
-#if FLAREPP_SCORE_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
   }
 
   // Keys j >= kvalid of the group get probability 0.
