@@ -33,7 +33,7 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get_workload", "make_inputs",
-           "make_random_inputs", "round_to_dtype", "DTYPES"]
+           "make_random_inputs", "make_simplified_inputs", "round_to_dtype", "DTYPES"]
 
 DTYPES = ("fp32", "bf16", "fp16")
 
@@ -178,6 +178,19 @@ def make_random_inputs(B, H, N, M, D, dtype, seed, scale=1.0, gate=None):
         g = np.broadcast_to(np.asarray(gate, dtype=np.float32), (H,)).copy()
     out = dict(q0=q0, q_fixed=q_fixed, gate=g.astype(np.float32), k0=k0, k=k, v=v)
     for name in ("q0", "q_fixed", "k0", "k", "v"):
+        out[name] = round_to_dtype(out[name], dtype)
+    out.update(dtype=dtype, B=B, H=H, N=N, M=M, D=D)
+    return out
+
+
+def make_simplified_inputs(B, H, N, M, D, dtype, seed, scale=1.0):
+    """Seeded iid N(0, scale^2) inputs of the simplified mixer: q0 [H,M,D] and
+    k0, v0, k, v [B,H,N,D], drawn in that order and rounded to ``dtype``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = dict(q0=_normal(rng, (H, M, D), scale))
+    for name in ("k0", "v0", "k", "v"):
+        out[name] = _normal(rng, (B, H, N, D), scale)
+    for name in ("q0", "k0", "v0", "k", "v"):
         out[name] = round_to_dtype(out[name], dtype)
     out.update(dtype=dtype, B=B, H=H, N=N, M=M, D=D)
     return out

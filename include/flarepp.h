@@ -137,6 +137,30 @@ int flarepp_mixer_fwd_timed(int64_t B, int64_t H, int64_t N, int64_t M, int64_t 
                             void* const* events);
 
 /*
+ * Simplified FLARE++ mixer forward (what the first preprint called FLARE++;
+ * issue #2024, "v1 vs. v2" and "Changes from v1 to v2": four input
+ * projections, so the synthesis has its own values v0, and no fixed
+ * reference or gate, so the routing queries are the synthesized ones;
+ * paper summary "FLARE++: Low-rank attention with dynamic attention
+ * routing", "Dynamic Query Synthesis"), scale 1/sqrt(D) throughout:
+ *   q    = softmax_rows(s q0 k0^T) v0          per (b, h)
+ *   z    = softmax_rows(s q k^T) v ;  y = softmax_rows(s k q^T) z.
+ *
+ *   q0      : [H, M, D] dtype  learned seeds
+ *   k0, v0  : [B, H, N, D]     synthesis keys and values (v0 == k0 is allowed
+ *                              and gives flarepp_mixer_fwd with q_fixed = 0
+ *                              and an open gate, g = +inf)
+ *   k, v    : [B, H, N, D]     keys and values of the input tokens
+ *   y       : [B, H, N, D]     output, written; must not overlap any input
+ *   workspace as for flarepp_mixer_fwd (the same size function applies).
+ * Errors as for flarepp_mixer_fwd.
+ */
+int simplified_flarepp_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                 int dtype, const void* q0, const void* k0, const void* v0,
+                                 const void* k, const void* v, void* y, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * Two-step FLARE mixer forward (FLARE.py README, section "FLARE"):
  *   z = softmax_rows(scale q k^T) v ;  y = softmax_rows(scale k q^T) z.
  * The listing on that page uses scale = 1.0; a closed-gate FLARE++ head

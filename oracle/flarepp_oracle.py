@@ -54,6 +54,7 @@ __all__ = [
     "decode_ref",
     "flare_ref",
     "flarepp_ref",
+    "simplified_flarepp_ref",
     "flarepp_head_intermediates",
     "synthesis_ref",
     "encode_partials_ref",
@@ -231,6 +232,30 @@ def flarepp_ref(q0, q_fixed, gate, k0, k, v, return_intermediates=False):
             zs[b, h] = z
     if return_intermediates:
         return y, dict(q=qs, z=zs)
+    return y
+
+
+def simplified_flarepp_ref(q0, k0, v0, k, v):
+    """Simplified FLARE++ (what the first preprint called FLARE++) in fp64.
+
+    Issue #2024, "v1 vs. v2" and "Changes from v1 to v2": four input
+    projections (the synthesis has its own values v0) and no fixed reference
+    or gate (the routing queries are the synthesized ones); the paper summary
+    "FLARE++: Low-rank attention with dynamic attention routing",
+    "Dynamic Query Synthesis": the seeds attend over the input tokens and the
+    M results serve as the routing queries of the FLARE encode-decode pair.
+    Per (b, h), s = 1/sqrt(D):
+      q = softmax(s q0 k0^T) v0;  z = softmax(s q k^T) v;  y = softmax(s k q^T) z.
+    q0: [H,M,D]; k0, v0, k, v: [B,H,N,D].
+    """
+    B, H, N, D = np.shape(k)
+    s = 1.0 / np.sqrt(D)
+    y = np.empty((B, H, N, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            q = attention(q0[h], k0[b, h], v0[b, h], s)
+            z = attention(q, k[b, h], v[b, h], s)
+            y[b, h] = attention(k[b, h], q, z, s)
     return y
 
 

@@ -9,6 +9,7 @@ library is missing, loading it raises.
 Entry points (same names as the C ABI in include/flarepp.h):
 
 * ``flarepp_mixer_fwd(q0, q_fixed, gate, k0, k, v)`` -> y
+* ``simplified_flarepp_mixer_fwd(q0, k0, v0, k, v)`` -> y
 * ``flare_mixer_fwd(q, k, v, scale)`` -> y
 * ``flare_encode_fwd(q, k, v, scale, chunk_tokens=0)`` -> z (fp32)
 * ``flare_decode_fwd(q, z, k, scale)`` -> y
@@ -24,7 +25,8 @@ import re
 
 __all__ = [
     "FlareppError", "load_library", "library_path", "dtype_code",
-    "flarepp_mixer_fwd", "flarepp_mixer_fwd_timed", "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
+    "flarepp_mixer_fwd", "flarepp_mixer_fwd_timed", "simplified_flarepp_mixer_fwd",
+    "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
     "flarepp_workspace_size", "flare_encode_workspace_size", "flare_decode_workspace_size",
     "flarepp_status_string", "flarepp_version", "declared_functions",
     "FLAREPP_OK", "FLAREPP_ERR_INVALID_ARGUMENT", "FLAREPP_ERR_UNSUPPORTED",
@@ -82,6 +84,8 @@ def load_library():
     lib.flarepp_mixer_fwd.restype = i32
     lib.flarepp_mixer_fwd_timed.argtypes = shape + [i32] + [vp] * 7 + [vp, sz, vp, vp]
     lib.flarepp_mixer_fwd_timed.restype = i32
+    lib.simplified_flarepp_mixer_fwd.argtypes = shape + [i32] + [vp] * 6 + [vp, sz, vp]
+    lib.simplified_flarepp_mixer_fwd.restype = i32
     lib.flare_mixer_fwd.argtypes = shape + [i32, f32] + [vp] * 4 + [vp, sz, vp]
     lib.flare_mixer_fwd.restype = i32
     lib.flare_encode_fwd.argtypes = shape + [i32, f32, vp, i64, vp, vp, vp, i64, vp, sz, vp]
@@ -97,7 +101,7 @@ def declared_functions():
     with open(_HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(flare\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(\w*flare\w*)\s*\(", text)))
 
 
 def flarepp_status_string(status: int) -> str:
@@ -193,6 +197,32 @@ def flarepp_mixer_fwd(q0, q_fixed, gate, k0, k, v, y=None, workspace=None, strea
     _call(lib.flarepp_mixer_fwd, "flarepp_mixer_fwd", B, H, N, M, D, code, _ptr(q0),
           _ptr(q_fixed), _ptr(gate), _ptr(k0), _ptr(k), _ptr(v), _ptr(y), _ptr(ws),
           ws.numel(), _stream(stream))
+    return y
+
+
+def simplified_flarepp_mixer_fwd(q0, k0, v0, k, v, y=None, workspace=None, stream=None):
+    """Simplified FLARE++ (separate synthesis values v0, q = synthesized
+    query); see include/flarepp.h.  Returns y."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q0.shape[1]
+    dev, dt = k.device, k.dtype
+    for name, t, shp in (("q0", q0, (H, M, D)), ("k0", k0, (B, H, N, D)),
+                         ("v0", v0, (B, H, N, D)), ("k", k, (B, H, N, D)),
+                         ("v", v, (B, H, N, D))):
+        _check_tensor(name, t, shp, dt, dev)
+    if y is None:
+        y = torch.empty((B, H, N, D), dtype=dt, device=dev)
+    _check_tensor("y", y, (B, H, N, D), dt, dev)
+    code = dtype_code(k)
+    nbytes = lib.flarepp_workspace_size(B, H, N, M, D, code)
+    if nbytes == 0:
+        raise FlareppError(FLAREPP_ERR_UNSUPPORTED, "flarepp_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    _call(lib.simplified_flarepp_mixer_fwd, "simplified_flarepp_mixer_fwd", B, H, N, M, D, code,
+          _ptr(q0), _ptr(k0), _ptr(v0), _ptr(k), _ptr(v), _ptr(y), _ptr(ws), ws.numel(),
+          _stream(stream))
     return y
 
 

@@ -205,19 +205,22 @@ hipError_t decode(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh
     if (e_ != hipSuccess) return FLAREPP_ERR_HIP; \
   } while (0)
 
+// FLARE++ (v0 == k0, q_fixed and gate given) and simplified FLARE++ (own
+// synthesis values v0, q_fixed == gate == NULL: q is the synthesized query).
 int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, const void* q0,
-               const void* q_fixed, const float* gate, const void* k0, const void* k,
-               const void* v, void* y, void* ws, size_t ws_bytes, void* stream,
+               const void* q_fixed, const float* gate, const void* k0, const void* v0,
+               const void* k, const void* v, void* y, void* ws, size_t ws_bytes, void* stream,
                void* const* events) {
-  if (!q0 || !q_fixed || !gate || !k0 || !k || !v || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
+  const bool simplified = q_fixed == nullptr && gate == nullptr;
+  if (!q0 || !k0 || !v0 || !k || !v || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
   Plan p;
   int st = make_plan(B, H, N, M, D, dtype, 0, &p);
   if (st != FLAREPP_OK) return st;
   const size_t tok = (size_t)(B * H * N * D) * esize_of(dtype);
   const size_t lat = (size_t)(H * M * D) * esize_of(dtype);
-  if (overlaps(y, tok, k0, tok) || overlaps(y, tok, k, tok) || overlaps(y, tok, v, tok) ||
-      overlaps(y, tok, q0, lat) || overlaps(y, tok, q_fixed, lat) ||
-      overlaps(y, tok, gate, (size_t)H * 4))
+  if (overlaps(y, tok, k0, tok) || overlaps(y, tok, v0, tok) || overlaps(y, tok, k, tok) ||
+      overlaps(y, tok, v, tok) || overlaps(y, tok, q0, lat) ||
+      (!simplified && (overlaps(y, tok, q_fixed, lat) || overlaps(y, tok, gate, (size_t)H * 4))))
     return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_workspace(p, ws, ws_bytes)) != FLAREPP_OK) return st;
   if ((st = check_device()) != FLAREPP_OK) return st;
@@ -234,9 +237,9 @@ int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   FLAREPP_TRY(prep_latents(p, ws, p.off_q0, q0, 0, (int)H, c, s));
   FLAREPP_TRY(mark(1));
   FLAREPP_TRY(launch_encode(dtype, (int)D,
-                            encode_params(p, ws, ws_at(ws, p.off_q0), 0, qh, k0, k0, gate), s));
+                            encode_params(p, ws, ws_at(ws, p.off_q0), 0, qh, k0, v0, gate), s));
   FLAREPP_TRY(mark(2));
-  // 3. q = q_fixed + sigma * q_dyn, per (b, h), as operand
+  // 3. q = q_fixed + sigma * q_dyn (simplified: q = q_dyn), per (b, h), as operand
   {
     CombineParams cp = combine_base(p, ws);
     cp.nsets = (int)BH;
@@ -330,7 +333,20 @@ int flarepp_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int
                       const void* k, const void* v, void* y, void* workspace,
                       size_t workspace_bytes, void* stream) {
   try {
-    return mixer_impl(B, H, N, M, D, dtype, q0, q_fixed, gate, k0, k, v, y, workspace,
+    if (!q_fixed || !gate) return FLAREPP_ERR_INVALID_ARGUMENT;
+    return mixer_impl(B, H, N, M, D, dtype, q0, q_fixed, gate, k0, k0, k, v, y, workspace,
+                      workspace_bytes, stream, nullptr);
+  } catch (...) {
+    return FLAREPP_ERR_HIP;
+  }
+}
+
+int simplified_flarepp_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                 int dtype, const void* q0, const void* k0, const void* v0,
+                                 const void* k, const void* v, void* y, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  try {
+    return mixer_impl(B, H, N, M, D, dtype, q0, nullptr, nullptr, k0, v0, k, v, y, workspace,
                       workspace_bytes, stream, nullptr);
   } catch (...) {
     return FLAREPP_ERR_HIP;
@@ -346,7 +362,8 @@ int flarepp_mixer_fwd_timed(int64_t B, int64_t H, int64_t N, int64_t M, int64_t 
     if (events == nullptr) return FLAREPP_ERR_INVALID_ARGUMENT;
     for (int i = 0; i < FLAREPP_TIMED_EVENTS; ++i)
       if (events[i] == nullptr) return FLAREPP_ERR_INVALID_ARGUMENT;
-    return mixer_impl(B, H, N, M, D, dtype, q0, q_fixed, gate, k0, k, v, y, workspace,
+    if (!q_fixed || !gate) return FLAREPP_ERR_INVALID_ARGUMENT;
+    return mixer_impl(B, H, N, M, D, dtype, q0, q_fixed, gate, k0, k0, k, v, y, workspace,
                       workspace_bytes, stream, events);
   } catch (...) {
     return FLAREPP_ERR_HIP;

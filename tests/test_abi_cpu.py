@@ -22,7 +22,7 @@ OK, INV, UNS, WS, HIP = (fp.FLAREPP_OK, fp.FLAREPP_ERR_INVALID_ARGUMENT,
 # fake, distinct, 256-aligned addresses: never dereferenced because every
 # call below fails validation (or the device check) before any launch
 FAKE = {name: ctypes.c_void_p(0x10000000 * (i + 1)) for i, name in
-        enumerate(["q0", "qf", "gate", "k0", "k", "v", "y", "ws", "z"])}
+        enumerate(["q0", "qf", "gate", "k0", "k", "v", "y", "ws", "z", "v0"])}
 
 
 def lib():
@@ -132,3 +132,34 @@ def test_encode_and_decode_seams_validate():
                               FAKE["k"], FAKE["ws"], wsd, None) == INV
     assert L.flare_decode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 0, None, FAKE["k"],
                               FAKE["y"], FAKE["ws"], wsd, None) == INV
+
+
+def _simplified(B=1, H=2, N=1024, M=16, D=8, dt=1, q0="q0", k0="k0", v0="v0", k="k", v="v",
+                y="y", ws="ws", wsb=None):
+    ptr = lambda n: None if n is None else FAKE[n]
+    if wsb is None:
+        wsb = fp.flarepp_workspace_size(B, H, N, M, D, dt) or 1 << 30
+    return lib().simplified_flarepp_mixer_fwd(B, H, N, M, D, dt, ptr(q0), ptr(k0), ptr(v0),
+                                              ptr(k), ptr(v), ptr(y), ptr(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q0=None), INV), (dict(k0=None), INV), (dict(v0=None), INV), (dict(k=None), INV),
+    (dict(v=None), INV), (dict(y=None), INV), (dict(M=0), INV), (dict(D=12), UNS),
+    (dict(ws=None), WS), (dict(wsb=1), WS), (dict(y="v0"), INV), (dict(y="k0"), INV),
+])
+def test_simplified_rejects_before_any_launch(kw, code):
+    assert _simplified(**kw) == code
+
+
+def test_flarepp_still_requires_fixed_queries_and_gate():
+    # null q_fixed or gate is an error for FLARE++ (not a silent switch to
+    # the simplified mixer)
+    assert _mixer(qf=None) == INV and _mixer(gate=None) == INV
+
+
+def test_simplified_valid_call_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert _simplified() == HIP

@@ -281,3 +281,36 @@ def test_decode_exact_recompute(fp, dtype, kind, amount):
     err = rel_err(y, ref)
     note(f"[decode recompute] {dtype} {kind} {amount} rel err {err:.3e}")
     assert err <= TOL[dtype]
+
+
+# ---------------------------------------------------------------------------
+# Simplified FLARE++ (separate synthesis values, q = synthesized query)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,N,M,D,dtype", [
+    (2, 4, 3000, 96, 32, "bf16"),
+    (1, 2, 1500, 64, 64, "fp16"),
+    (1, 2, 700, 40, 16, "fp32"),
+])
+def test_simplified_mixer_vs_oracle(fp, B, H, N, M, D, dtype):
+    from flarepp_workloads import make_simplified_inputs
+    note(f"[simplified] B{B} H{H} N{N} M{M} D{D} {dtype}")
+    x = make_simplified_inputs(B, H, N, M, D, dtype, seed=300 + N)
+    d = {n: torch.from_numpy(x[n]).to(TDT[dtype]).cuda() for n in ("q0", "k0", "v0", "k", "v")}
+    y = fp.simplified_flarepp_mixer_fwd(d["q0"], d["k0"], d["v0"], d["k"], d["v"])
+    torch.cuda.synchronize()
+    ref = oracle.simplified_flarepp_ref(*(x[n].astype(np.float64) for n in ("q0", "k0", "v0", "k", "v")))
+    err = rel_err(y.float().cpu().numpy(), ref)
+    note(f"[simplified] rel err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_simplified_with_shared_values_equals_open_gate_flarepp(fp, dtype):
+    x = make_random_inputs(2, 3, 2000, 64, 32, dtype, seed=8, gate=math.inf)
+    d = to_dev(x, dtype)
+    zeros = torch.zeros_like(d["q_fixed"])
+    y1 = fp.flarepp_mixer_fwd(d["q0"], zeros, d["gate"], d["k0"], d["k"], d["v"])
+    y2 = fp.simplified_flarepp_mixer_fwd(d["q0"], d["k0"], d["k0"], d["k"], d["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)

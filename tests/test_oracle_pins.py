@@ -453,3 +453,72 @@ def test_tiny_workload_oracle_against_torch():
     x = make_inputs("tiny_fp32")
     xs = {n: x[n].astype(np.float64) for n in ("q0", "q_fixed", "gate", "k0", "k", "v")}
     assert _rel(oracle.flarepp_ref(**xs), _torch_flarepp(**xs)) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Simplified FLARE++ (separate synthesis values, q = synthesized query)
+# ---------------------------------------------------------------------------
+
+def _srand(B, H, N, M, D, seed):
+    from flarepp_workloads import make_simplified_inputs
+    x = make_simplified_inputs(B, H, N, M, D, "fp32", seed)
+    return {n: x[n].astype(np.float64) for n in ("q0", "k0", "v0", "k", "v")}
+
+
+def _torch_simplified(q0, k0, v0, k, v):
+    T = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    kt, vt = T(k), T(v)
+    q0t = T(q0).unsqueeze(0).expand(kt.shape[0], -1, -1, -1).contiguous()
+    q = _torch_sdpa(q0t, T(k0), T(v0))
+    z = _torch_sdpa(q, kt, vt)
+    return _torch_sdpa(kt, q, z).numpy()
+
+
+def _brute_simplified(q0, k0, v0, k, v):
+    B, H, N, D = np.shape(k)
+    s = 1.0 / math.sqrt(D)
+    y = np.zeros((B, H, N, D))
+    L = lambda a: np.asarray(a, float).tolist()
+    for b in range(B):
+        for h in range(H):
+            q = _brute_attention(L(q0[h]), L(k0[b, h]), L(v0[b, h]), s)
+            z = _brute_attention(q, L(k[b, h]), L(v[b, h]), s)
+            y[b, h] = np.array(_brute_attention(L(k[b, h]), q, z, s))
+    return y
+
+
+def test_simplified_with_shared_values_is_open_gate_flarepp():
+    # v0 = k0, q_fixed = 0 and g = +inf (sigma = 1) give the same operations
+    x = _srand(2, 2, 40, 6, 4, 61)
+    y = oracle.simplified_flarepp_ref(x["q0"], x["k0"], x["k0"], x["k"], x["v"])
+    yp = oracle.flarepp_ref(x["q0"], np.zeros_like(x["q0"]), np.full(2, np.inf), x["k0"],
+                            x["k"], x["v"])
+    assert _rel(y, yp) <= 1e-15
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 37, 5, 4), (1, 2, 64, 8, 8), (3, 1, 19, 19, 3)])
+def test_simplified_vs_torch(shape):
+    x = _srand(*shape, seed=62)
+    assert _rel(oracle.simplified_flarepp_ref(**x), _torch_simplified(**x)) <= 1e-12
+
+
+def test_simplified_vs_brute_force():
+    for shape, seed in (((1, 1, 6, 2, 2), 63), ((2, 2, 5, 3, 1), 64)):
+        x = _srand(*shape, seed=seed)
+        assert _rel(oracle.simplified_flarepp_ref(**x), _brute_simplified(**x)) <= 1e-14
+
+
+def test_simplified_closed_forms():
+    x = _srand(2, 2, 1, 4, 3, 65)   # one token: every softmax is 1, y = v
+    assert _rel(oracle.simplified_flarepp_ref(**x), x["v"]) <= 1e-14
+    x = _srand(1, 2, 30, 5, 4, 66)  # constant values: y is that constant
+    x["v"] = np.full_like(x["v"], -2.5)
+    assert _rel(oracle.simplified_flarepp_ref(**x), x["v"]) <= 1e-14
+
+
+def test_simplified_synthesis_value_matters():
+    # a copy that ignores v0 (uses k0 as the synthesis value) must fail the
+    # library pin: the pins above see the separate synthesis values
+    x = _srand(2, 2, 30, 5, 4, 67)
+    wrong = oracle.simplified_flarepp_ref(x["q0"], x["k0"], x["k0"], x["k"], x["v"])
+    assert _rel(wrong, _torch_simplified(**x)) > 1e-6
