@@ -1,8 +1,12 @@
-"""fp64 CPU oracle for the FLARE++ mixer forward pass.
+"""fp64 CPU oracle for the FLARE++ mixer forward pass and its gradients.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check in
 __graft_entry__ and by the CPU-baseline leg of bench.py, never by the GPU
 library or its Python binding.
 """
 from .flarepp_oracle import *  # noqa: F401,F403
-from .flarepp_oracle import __all__  # noqa: F401
+from .flarepp_backward import *  # noqa: F401,F403
+from .flarepp_oracle import __all__ as _fwd_all
+from .flarepp_backward import __all__ as _bwd_all
+
+__all__ = list(_fwd_all) + list(_bwd_all)
