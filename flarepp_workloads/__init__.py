@@ -194,3 +194,10 @@ def make_simplified_inputs(B, H, N, M, D, dtype, seed, scale=1.0):
         out[name] = round_to_dtype(out[name], dtype)
     out.update(dtype=dtype, B=B, H=H, N=N, M=M, D=D)
     return out
+
+
+def make_cotangent(B, H, N, D, dtype, seed, scale=1.0):
+    """Seeded output gradient dy ~ iid N(0, scale^2) [B,H,N,D], rounded to
+    ``dtype`` (float32 array holding dtype-exact values)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return round_to_dtype(_normal(rng, (B, H, N, D), scale), dtype)

@@ -221,6 +221,73 @@ int flare_decode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
                      const void* k, void* y, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* ------------------------------------------------------------------------
+ * Training: forward with saved tensors, and the backward pass.
+ *
+ * The gradients follow from the forward definition by the chain rule (the
+ * pages state that the token-sharded encoder has a custom backward, issue
+ * #2024 "Multi-GPU context parallelism", but do not print it).  For one
+ * attention O = softmax_rows(s Q K^T) V with output gradient dO:
+ *   dV = A^T dO,  dS = A * (dO V^T - rowsum(dO * O)),  dQ = s dS K,
+ *   dK = s dS^T Q.
+ * The backward supports bf16 and fp16 with D in {16, 32, 64} (M <= 512;
+ * D = 64 needs M <= 416, all latents of a head held in one workgroup's
+ * 160 KiB LDS); other cases return FLAREPP_ERR_UNSUPPORTED.  The token
+ * tensors k, v, k0, y, dy and every gradient output (fp32) must be 16-byte
+ * aligned, else FLAREPP_ERR_INVALID_ARGUMENT.  Gradient outputs must not
+ * overlap any input or `saved`.  Results are deterministic (fixed reduction
+ * orders).  Calls run asynchronously on `stream`.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of the `saved` buffer a training forward fills (fp32): the routing
+ * query q [B,H,M,D], z [B,H,M,D], q_dyn [B,H,M,D], the base-2 log-sum-exp of
+ * the synthesis and encoder rows [B,H,M] each and of the decoder rows
+ * [B,H,N].  0 for invalid sizes. */
+size_t flarepp_saved_size(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D);
+
+/* flarepp_mixer_fwd that also fills `saved` (>= flarepp_saved_size bytes,
+ * 16-byte aligned, caller-owned, must not overlap y or the workspace). */
+int flarepp_mixer_fwd_train(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                            const void* q0, const void* q_fixed, const float* gate,
+                            const void* k0, const void* k, const void* v, void* y, float* saved,
+                            size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* flare_mixer_fwd that also fills `saved` (z and the encoder and decoder
+ * log-sum-exp rows; the q and q_dyn slots are left untouched). */
+int flare_mixer_fwd_train(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                          float scale, const void* q, const void* k, const void* v, void* y,
+                          float* saved, size_t saved_bytes, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of flarepp_mixer_bwd / flare_mixer_bwd (256-byte aligned);
+ * 0 for unsupported or invalid arguments. */
+size_t flarepp_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                  int dtype);
+
+/*
+ * FLARE++ backward.  Inputs as for flarepp_mixer_fwd plus the forward's
+ * output y and the output gradient dy [B,H,N,D] (dtype), and `saved` from
+ * flarepp_mixer_fwd_train on the same inputs.  Writes (fp32):
+ *   dq0, dq_fixed : [H, M, D]   (summed over the batch)
+ *   dgate         : [H]         (gradient w.r.t. the gate LOGITS)
+ *   dk0, dk, dv   : [B, H, N, D]
+ * A closed gate (g = -inf) gives zero dq0, dk0 and dgate for its head.
+ */
+int flarepp_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                      const void* q0, const void* q_fixed, const float* gate, const void* k0,
+                      const void* k, const void* v, const void* y, const void* dy,
+                      const float* saved, size_t saved_bytes, float* dq0, float* dq_fixed,
+                      float* dgate, float* dk0, float* dk, float* dv, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* FLARE backward with the caller's scale; `saved` from flare_mixer_fwd_train.
+ * Writes dq [H, M, D] (summed over the batch), dk, dv [B, H, N, D] (fp32). */
+int flare_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                    float scale, const void* q, const void* k, const void* v, const void* y,
+                    const void* dy, const float* saved, size_t saved_bytes, float* dq, float* dk,
+                    float* dv, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

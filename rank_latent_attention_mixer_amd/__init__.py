@@ -11,6 +11,8 @@ Entry points (same names as the C ABI in include/flarepp.h):
 * ``flarepp_mixer_fwd(q0, q_fixed, gate, k0, k, v)`` -> y
 * ``simplified_flarepp_mixer_fwd(q0, k0, v0, k, v)`` -> y
 * ``flare_mixer_fwd(q, k, v, scale)`` -> y
+* ``flarepp_mixer_fwd_train(...)`` -> (y, saved); ``flarepp_mixer_bwd(..., y, dy, saved)``
+  -> dict of fp32 gradients; ``flare_mixer_fwd_train`` / ``flare_mixer_bwd`` likewise
 * ``flare_encode_fwd(q, k, v, scale, chunk_tokens=0)`` -> z (fp32)
 * ``flare_decode_fwd(q, z, k, scale)`` -> y
 * ``flarepp_workspace_size(B, H, N, M, D, dtype)`` and friends
@@ -27,6 +29,7 @@ __all__ = [
     "FlareppError", "load_library", "library_path", "dtype_code",
     "flarepp_mixer_fwd", "flarepp_mixer_fwd_timed", "simplified_flarepp_mixer_fwd",
     "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
+    "flarepp_mixer_fwd_train", "flarepp_mixer_bwd", "flare_mixer_fwd_train", "flare_mixer_bwd",
     "flarepp_workspace_size", "flare_encode_workspace_size", "flare_decode_workspace_size",
     "flarepp_status_string", "flarepp_version", "declared_functions",
     "FLAREPP_OK", "FLAREPP_ERR_INVALID_ARGUMENT", "FLAREPP_ERR_UNSUPPORTED",
@@ -86,6 +89,18 @@ def load_library():
     lib.flarepp_mixer_fwd_timed.restype = i32
     lib.simplified_flarepp_mixer_fwd.argtypes = shape + [i32] + [vp] * 6 + [vp, sz, vp]
     lib.simplified_flarepp_mixer_fwd.restype = i32
+    lib.flarepp_saved_size.argtypes = shape
+    lib.flarepp_saved_size.restype = sz
+    lib.flarepp_mixer_fwd_train.argtypes = shape + [i32] + [vp] * 7 + [vp, sz, vp, sz, vp]
+    lib.flarepp_mixer_fwd_train.restype = i32
+    lib.flare_mixer_fwd_train.argtypes = shape + [i32, f32] + [vp] * 4 + [vp, sz, vp, sz, vp]
+    lib.flare_mixer_fwd_train.restype = i32
+    lib.flarepp_bwd_workspace_size.argtypes = shape + [i32]
+    lib.flarepp_bwd_workspace_size.restype = sz
+    lib.flarepp_mixer_bwd.argtypes = shape + [i32] + [vp] * 8 + [vp, sz] + [vp] * 6 + [vp, sz, vp]
+    lib.flarepp_mixer_bwd.restype = i32
+    lib.flare_mixer_bwd.argtypes = shape + [i32, f32] + [vp] * 5 + [vp, sz] + [vp] * 3 + [vp, sz, vp]
+    lib.flare_mixer_bwd.restype = i32
     lib.flare_mixer_fwd.argtypes = shape + [i32, f32] + [vp] * 4 + [vp, sz, vp]
     lib.flare_mixer_fwd.restype = i32
     lib.flare_encode_fwd.argtypes = shape + [i32, f32, vp, i64, vp, vp, vp, i64, vp, sz, vp]
@@ -336,3 +351,112 @@ def flare_decode_fwd(q, z, k, scale, y=None, workspace=None, stream=None):
 
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
+
+
+# --------------------------------------------------------------------------
+# training: forward with saved tensors, backward
+# --------------------------------------------------------------------------
+
+def _saved_buffer(B, H, N, M, D, device):
+    import torch
+    n = load_library().flarepp_saved_size(B, H, N, M, D)
+    if n == 0:
+        raise FlareppError(FLAREPP_ERR_INVALID_ARGUMENT, "flarepp_saved_size")
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def flarepp_mixer_fwd_train(q0, q_fixed, gate, k0, k, v, y=None, workspace=None, stream=None):
+    """FLARE++ forward that also returns the tensors its backward needs."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q0.shape[1]
+    dev, dt = k.device, k.dtype
+    for name, t, shp in (("q0", q0, (H, M, D)), ("q_fixed", q_fixed, (H, M, D)),
+                         ("k0", k0, (B, H, N, D)), ("k", k, (B, H, N, D)),
+                         ("v", v, (B, H, N, D))):
+        _check_tensor(name, t, shp, dt, dev)
+    _check_tensor("gate", gate, (H,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, H, N, D), dtype=dt, device=dev)
+    _check_tensor("y", y, (B, H, N, D), dt, dev)
+    saved = _saved_buffer(B, H, N, M, D, dev)
+    code = dtype_code(k)
+    ws = _workspace(lib.flarepp_workspace_size(B, H, N, M, D, code), dev, workspace)
+    _call(lib.flarepp_mixer_fwd_train, "flarepp_mixer_fwd_train", B, H, N, M, D, code, _ptr(q0),
+          _ptr(q_fixed), _ptr(gate), _ptr(k0), _ptr(k), _ptr(v), _ptr(y), _ptr(saved),
+          saved.numel() * 4, _ptr(ws), ws.numel(), _stream(stream))
+    return y, saved
+
+
+def flarepp_mixer_bwd(q0, q_fixed, gate, k0, k, v, y, dy, saved, workspace=None, stream=None):
+    """Gradients of the FLARE++ mixer (fp32): dict(dq0, dq_fixed, dgate, dk0, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q0.shape[1]
+    dev, dt = k.device, k.dtype
+    for name, t, shp in (("q0", q0, (H, M, D)), ("q_fixed", q_fixed, (H, M, D)),
+                         ("k0", k0, (B, H, N, D)), ("k", k, (B, H, N, D)),
+                         ("v", v, (B, H, N, D)), ("y", y, (B, H, N, D)),
+                         ("dy", dy, (B, H, N, D))):
+        _check_tensor(name, t, shp, dt, dev)
+    _check_tensor("gate", gate, (H,), torch.float32, dev)
+    f = dict(device=dev, dtype=torch.float32)
+    g = dict(dq0=torch.empty((H, M, D), **f), dq_fixed=torch.empty((H, M, D), **f),
+             dgate=torch.empty((H,), **f), dk0=torch.empty((B, H, N, D), **f),
+             dk=torch.empty((B, H, N, D), **f), dv=torch.empty((B, H, N, D), **f))
+    code = dtype_code(k)
+    nbytes = lib.flarepp_bwd_workspace_size(B, H, N, M, D, code)
+    if nbytes == 0:
+        raise FlareppError(FLAREPP_ERR_UNSUPPORTED, "flarepp_bwd_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    _call(lib.flarepp_mixer_bwd, "flarepp_mixer_bwd", B, H, N, M, D, code, _ptr(q0),
+          _ptr(q_fixed), _ptr(gate), _ptr(k0), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(saved),
+          saved.numel() * 4, _ptr(g["dq0"]), _ptr(g["dq_fixed"]), _ptr(g["dgate"]),
+          _ptr(g["dk0"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(ws), ws.numel(), _stream(stream))
+    return g
+
+
+def flare_mixer_fwd_train(q, k, v, scale, y=None, workspace=None, stream=None):
+    """FLARE forward that also returns the tensors its backward needs."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q.shape[1]
+    dev, dt = k.device, k.dtype
+    for name, t, shp in (("q", q, (H, M, D)), ("k", k, (B, H, N, D)), ("v", v, (B, H, N, D))):
+        _check_tensor(name, t, shp, dt, dev)
+    if y is None:
+        y = torch.empty((B, H, N, D), dtype=dt, device=dev)
+    saved = _saved_buffer(B, H, N, M, D, dev)
+    code = dtype_code(k)
+    ws = _workspace(lib.flarepp_workspace_size(B, H, N, M, D, code), dev, workspace)
+    _call(lib.flare_mixer_fwd_train, "flare_mixer_fwd_train", B, H, N, M, D, code, float(scale),
+          _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(saved), saved.numel() * 4, _ptr(ws),
+          ws.numel(), _stream(stream))
+    return y, saved
+
+
+def flare_mixer_bwd(q, k, v, scale, y, dy, saved, workspace=None, stream=None):
+    """Gradients of the FLARE mixer (fp32): dict(dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q.shape[1]
+    dev, dt = k.device, k.dtype
+    for name, t, shp in (("q", q, (H, M, D)), ("k", k, (B, H, N, D)), ("v", v, (B, H, N, D)),
+                         ("y", y, (B, H, N, D)), ("dy", dy, (B, H, N, D))):
+        _check_tensor(name, t, shp, dt, dev)
+    f = dict(device=dev, dtype=torch.float32)
+    g = dict(dq=torch.empty((H, M, D), **f), dk=torch.empty((B, H, N, D), **f),
+             dv=torch.empty((B, H, N, D), **f))
+    code = dtype_code(k)
+    nbytes = lib.flarepp_bwd_workspace_size(B, H, N, M, D, code)
+    if nbytes == 0:
+        raise FlareppError(FLAREPP_ERR_UNSUPPORTED, "flarepp_bwd_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    _call(lib.flare_mixer_bwd, "flare_mixer_bwd", B, H, N, M, D, code, float(scale), _ptr(q),
+          _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(saved), saved.numel() * 4, _ptr(g["dq"]),
+          _ptr(g["dk"]), _ptr(g["dv"]), _ptr(ws), ws.numel(), _stream(stream))
+    return g

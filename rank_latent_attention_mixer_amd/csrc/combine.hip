@@ -57,6 +57,9 @@ __device__ __forceinline__ Lse lse_merge(const Lse& a, const Lse& b) {
   return r;
 }
 
+// Base-2 log-sum-exp of a merged state: m + log2(l).
+__device__ __forceinline__ float lse_state_base2(float m, float l) { return m + log2f(l); }
+
 // One thread per (latent set, latent m, 4 output columns, chunk quarter):
 // each of the four lanes of a slot merges every fourth chunk, then the
 // lanes combine in a fixed butterfly and the first lane writes.
@@ -80,6 +83,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
   }
 
   f32x4 merged = {0.f, 0.f, 0.f, 0.f};
+  float lse_m = 0.f, lse_l = 1.f;
   if (use_parts) {  // uniform over the grid
     Lse st{-__builtin_inff(), 0.f, {0.f, 0.f, 0.f, 0.f}};
     if (live) {
@@ -104,11 +108,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
       st = lse_merge(st, o);
     }
     merged = st.o / st.l;
+    lse_m = st.m;
+    lse_l = st.l;
   }
   if (!in_range || quarter != 0) return;
 
   float val[4] = {0.f, 0.f, 0.f, 0.f};
   if (live) {
+    const int64_t ri = ((int64_t)set * a.M + m) * a.D + d0;  // natural [sets][M][D]
+    if (a.lse_out && d0 == 0)
+      a.lse_out[(int64_t)set * a.M + m] = use_parts ? lse_state_base2(lse_m, lse_l) : 0.f;
     if (a.mode == kModeQuery) {
       const int b = set / a.H;
 #pragma unroll
@@ -117,7 +126,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
             a.fixed ? load_as_float(a.fixed, b * a.fixed_b_stride + ((int64_t)h * a.M + m) * a.D + d0 + e,
                                     a.fixed_dtype)
                     : 0.f;
-        val[e] = (use_parts ? fmaf(sg, merged[e], fx) : fx) * a.cscale;
+        const float qv = use_parts ? fmaf(sg, merged[e], fx) : fx;
+        if (a.q_out) a.q_out[ri + e] = qv;
+        if (a.dyn_out) a.dyn_out[ri + e] = use_parts ? merged[e] : 0.f;
+        val[e] = qv * a.cscale;
       }
     } else {
       const int64_t zi = ((int64_t)set * a.M + m) * a.D + d0;

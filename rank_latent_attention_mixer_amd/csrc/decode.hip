@@ -211,8 +211,11 @@ decode_kernel(DecodeParams a) {
     auto store = [&](const auto& t) {
 #pragma unroll
       for (int cb = 0; cb < kNC; ++cb) {
-        const float inv = 1.0f / t.row_sum(cb);
+        const float l = t.row_sum(cb);
+        const float inv = 1.0f / l;
         const int64_t n = nb + cb * 32 + r;
+        if (a.lse_out && h == 0 && n < a.N)  // saved for the backward pass
+          a.lse_out[(int64_t)bh * a.N + n] = log2f(l) + t.reference(cb);
         if (n < a.N) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
@@ -352,6 +355,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams a) {
   if (valid) {
     float* yb = reinterpret_cast<float*>(a.y) + (int64_t)bh * a.N * D;
     const float inv = 1.0f / l;
+    if (a.lse_out) a.lse_out[(int64_t)bh * a.N + n] = mref + log2f(l);
 #pragma unroll
     for (int d = 0; d < D; ++d) yb[n * D + d] = o[d] * inv;
   }

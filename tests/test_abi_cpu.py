@@ -163,3 +163,78 @@ def test_simplified_valid_call_without_device_reports_hip_error():
     if torch.cuda.is_available():
         pytest.skip("a device is present")
     assert _simplified() == HIP
+
+
+# ---------------------------------------------------------------- backward
+GRADS = {name: ctypes.c_void_p(0x10000000 * (i + 20)) for i, name in
+         enumerate(["dq0", "dqf", "dgate", "dk0", "dk", "dv", "saved", "dy", "bws"])}
+
+
+def test_saved_size_formula():
+    B, H, N, M, D = 2, 3, 1000, 40, 32
+    assert lib().flarepp_saved_size(B, H, N, M, D) == 4 * (3 * B * H * M * D + 2 * B * H * M + B * H * N)
+    assert lib().flarepp_saved_size(0, 1, 1, 1, 16) == 0
+
+
+@pytest.mark.parametrize("args,ok", [
+    ((1, 8, 1 << 20, 512, 32, 1), True),
+    ((2, 2, 700, 80, 16, 2), True),
+    ((1, 1, 100, 416, 64, 1), True),
+    ((1, 1, 100, 448, 64, 1), False),    # latents of a head exceed the LDS
+    ((1, 1, 100, 64, 8, 1), False),      # D = 8: no matrix-core backward
+    ((1, 1, 100, 64, 32, 0), False),     # fp32
+    ((1, 1, 0, 64, 32, 1), False),
+])
+def test_bwd_workspace_size(args, ok):
+    assert (fp.load_library().flarepp_bwd_workspace_size(*args) > 0) == ok
+
+
+def _bwd(B=1, H=2, N=1024, M=16, D=32, dt=1, saved_bytes=None, wsb=None, **kw):
+    names = dict(q0="q0", qf="qf", gate="gate", k0="k0", k="k", v="v", y="y", dy="dy",
+                 saved="saved", dq0="dq0", dqf="dqf", dgate="dgate", dk0="dk0", dk="dk",
+                 dv="dv", ws="bws")
+    names.update(kw)
+    ptr = lambda n: None if n is None else (n if isinstance(n, ctypes.c_void_p)
+                                            else FAKE.get(n) or GRADS[n])
+    if saved_bytes is None:
+        saved_bytes = lib().flarepp_saved_size(B, H, N, M, D)
+    if wsb is None:
+        wsb = fp.load_library().flarepp_bwd_workspace_size(B, H, N, M, D, dt) or 1 << 30
+    n = names
+    return lib().flarepp_mixer_bwd(B, H, N, M, D, dt, ptr(n["q0"]), ptr(n["qf"]), ptr(n["gate"]),
+                                   ptr(n["k0"]), ptr(n["k"]), ptr(n["v"]), ptr(n["y"]),
+                                   ptr(n["dy"]), ptr(n["saved"]), saved_bytes, ptr(n["dq0"]),
+                                   ptr(n["dqf"]), ptr(n["dgate"]), ptr(n["dk0"]), ptr(n["dk"]),
+                                   ptr(n["dv"]), ptr(n["ws"]), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q0=None), INV), (dict(gate=None), INV), (dict(k0=None), INV), (dict(k=None), INV),
+    (dict(y=None), INV), (dict(dy=None), INV), (dict(saved=None), INV), (dict(dq0=None), INV),
+    (dict(dqf=None), INV), (dict(dgate=None), INV), (dict(dk0=None), INV), (dict(dk=None), INV),
+    (dict(dv=None), INV), (dict(D=8), UNS), (dict(dt=0), UNS), (dict(M=448, D=64), UNS),
+    (dict(saved_bytes=64), WS), (dict(ws=None), WS), (dict(wsb=1), WS),
+    (dict(dk="k"), INV), (dict(dv="dy"), INV), (dict(dk0="saved"), INV),
+    (dict(dy=ctypes.c_void_p(0x10000000 * 27 + 8)), INV),       # misaligned dy
+    (dict(dk=ctypes.c_void_p(0x10000000 * 24 + 4)), INV),       # misaligned dk
+])
+def test_bwd_rejects_before_any_launch(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_bwd_valid_call_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert _bwd() == HIP
+
+
+def test_fwd_train_rejects_small_saved_buffer():
+    B, H, N, M, D, dt = 1, 2, 1024, 16, 32, 1
+    L = lib()
+    ws = fp.flarepp_workspace_size(B, H, N, M, D, dt)
+    args = [FAKE[n] for n in ("q0", "qf", "gate", "k0", "k", "v", "y")]
+    assert L.flarepp_mixer_fwd_train(B, H, N, M, D, dt, *args, GRADS["saved"], 64, FAKE["ws"],
+                                     ws, None) == WS
+    assert L.flare_mixer_fwd_train(B, H, N, M, D, dt, 0.5, FAKE["q0"], FAKE["k"], FAKE["v"],
+                                   FAKE["y"], GRADS["saved"], 64, FAKE["ws"], ws, None) == WS
