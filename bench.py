@@ -10,6 +10,9 @@ Prints one JSON line on stdout; progress goes to stderr.
                   [--cpu-seconds S | --no-cpu-baseline]
   python bench.py --copy-calibration-mib S   (plain device copy of S MiB, for
                                               scaling the HBM byte counters)
+  python bench.py --backward [--steps K] [--warmup W] [--workload NAME]
+                  (times flarepp_mixer_bwd alone: one training forward fills
+                   the saved tensors, then K backward calls are timed)
 """
 
 from __future__ import annotations
@@ -160,6 +163,59 @@ def cpu_baseline(x, w, seconds):
             "blas": blas}
 
 
+def bench_backward(a, fp, torch, np, w, x, args, y, ws):
+    """Times K flarepp_mixer_bwd calls on the saved tensors of one training
+    forward; prints one JSON line."""
+    from flarepp_workloads import make_cotangent
+    dev = y.device
+    tdt = y.dtype
+    dy = torch.from_numpy(make_cotangent(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed + 100))
+    dy = dy.to(dev).to(tdt)
+    y, saved = fp.flarepp_mixer_fwd_train(*args, y=y, workspace=ws)
+    code = fp.dtype_code(y)
+    nbytes = fp.load_library().flarepp_bwd_workspace_size(w.B, w.H, w.N, w.M, w.D, code)
+    bws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] backward: saved {saved.numel() * 4 / 2**20:.1f} MiB, "
+        f"workspace {nbytes / 2**20:.1f} MiB")
+    for _ in range(a.warmup):
+        g = fp.flarepp_mixer_bwd(*args, y, dy, saved, workspace=bws)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(a.steps):
+        g = fp.flarepp_mixer_bwd(*args, y, dy, saved, workspace=bws)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / a.steps
+    for n, t in g.items():
+        if not bool(torch.isfinite(t).all()):
+            log(f"[bench] non-finite gradient {n}")
+            return 1
+    sig = 1.0 / (1.0 + np.exp(-x["gate"].astype(np.float64)))
+    # five products per attention backward (S, dP, dV, dQ, dK), 2 flops per
+    # multiply-add; the synthesis only where the gate is open
+    attn = sum((3 if s > 0 else 2) for s in sig)
+    flops = 5 * 2 * attn * w.B * w.N * w.M * w.D
+    t = ms_per_step / 1e3
+    result = {
+        "metric": "FLARE++ mixer bwd tokens/s & TFLOP/s (%bf16 MFMA peak), 1 GPU",
+        "value": round(w.B * w.N / t, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D,
+                   "dtype": w.dtype, "global_batch": w.B, "seq_len": w.N,
+                   "parallelism": "single-gpu", "pass": "backward"},
+        "tflops": round(flops / t / 1e12, 2),
+        "frac_bf16_peak": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +225,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--backward", action="store_true")
     a = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -208,6 +265,8 @@ def main(argv=None):
     log(f"[bench] inputs resident ({time.perf_counter() - t0:.1f}s)")
 
     args = (d["q0"], d["q_fixed"], d["gate"], d["k0"], d["k"], d["v"])
+    if a.backward:
+        return bench_backward(a, fp, torch, np, w, x, args, y, ws)
     for _ in range(a.warmup):
         fp.flarepp_mixer_fwd(*args, y=y, workspace=ws)
     torch.cuda.synchronize()

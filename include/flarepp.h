@@ -288,6 +288,29 @@ int flare_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int d
                     const void* dy, const float* saved, size_t saved_bytes, float* dq, float* dk,
                     float* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/* simplified_flarepp_mixer_fwd that also fills `saved` (the q slot holds
+ * the synthesized query q = q_dyn). */
+int simplified_flarepp_mixer_fwd_train(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                       int dtype, const void* q0, const void* k0, const void* v0,
+                                       const void* k, const void* v, void* y, float* saved,
+                                       size_t saved_bytes, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the simplified mixer (issue #2024, "Changes from v1 to v2":
+ * the v1 form, q = softmax(s q0 k0^T) v0 with its own synthesis values).
+ * `saved` from simplified_flarepp_mixer_fwd_train on the same inputs.
+ * Writes (fp32): dq0 [H, M, D] (summed over the batch), dk0, dv0, dk, dv
+ * [B, H, N, D].  v0 == k0 is rejected (that is FLARE++ with an open gate and
+ * no fixed queries; use flarepp_mixer_bwd).  Other rules as flarepp_mixer_bwd.
+ */
+int simplified_flarepp_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                 int dtype, const void* q0, const void* k0, const void* v0,
+                                 const void* k, const void* v, const void* y, const void* dy,
+                                 const float* saved, size_t saved_bytes, float* dq0, float* dk0,
+                                 float* dv0, float* dk, float* dv, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

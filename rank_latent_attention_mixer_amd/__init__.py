@@ -30,6 +30,7 @@ __all__ = [
     "flarepp_mixer_fwd", "flarepp_mixer_fwd_timed", "simplified_flarepp_mixer_fwd",
     "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
     "flarepp_mixer_fwd_train", "flarepp_mixer_bwd", "flare_mixer_fwd_train", "flare_mixer_bwd",
+    "simplified_flarepp_mixer_fwd_train", "simplified_flarepp_mixer_bwd",
     "flarepp_workspace_size", "flare_encode_workspace_size", "flare_decode_workspace_size",
     "flarepp_status_string", "flarepp_version", "declared_functions",
     "FLAREPP_OK", "FLAREPP_ERR_INVALID_ARGUMENT", "FLAREPP_ERR_UNSUPPORTED",
@@ -101,6 +102,10 @@ def load_library():
     lib.flarepp_mixer_bwd.restype = i32
     lib.flare_mixer_bwd.argtypes = shape + [i32, f32] + [vp] * 5 + [vp, sz] + [vp] * 3 + [vp, sz, vp]
     lib.flare_mixer_bwd.restype = i32
+    lib.simplified_flarepp_mixer_fwd_train.argtypes = shape + [i32] + [vp] * 6 + [vp, sz, vp, sz, vp]
+    lib.simplified_flarepp_mixer_fwd_train.restype = i32
+    lib.simplified_flarepp_mixer_bwd.argtypes = shape + [i32] + [vp] * 7 + [vp, sz] + [vp] * 5 + [vp, sz, vp]
+    lib.simplified_flarepp_mixer_bwd.restype = i32
     lib.flare_mixer_fwd.argtypes = shape + [i32, f32] + [vp] * 4 + [vp, sz, vp]
     lib.flare_mixer_fwd.restype = i32
     lib.flare_encode_fwd.argtypes = shape + [i32, f32, vp, i64, vp, vp, vp, i64, vp, sz, vp]
@@ -459,4 +464,51 @@ def flare_mixer_bwd(q, k, v, scale, y, dy, saved, workspace=None, stream=None):
     _call(lib.flare_mixer_bwd, "flare_mixer_bwd", B, H, N, M, D, code, float(scale), _ptr(q),
           _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(saved), saved.numel() * 4, _ptr(g["dq"]),
           _ptr(g["dk"]), _ptr(g["dv"]), _ptr(ws), ws.numel(), _stream(stream))
+    return g
+
+
+def simplified_flarepp_mixer_fwd_train(q0, k0, v0, k, v, y=None, workspace=None, stream=None):
+    """Simplified-mixer forward that also returns the tensors its backward needs."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q0.shape[1]
+    dev, dt = k.device, k.dtype
+    _check_tensor("q0", q0, (H, M, D), dt, dev)
+    for name, t in (("k0", k0), ("v0", v0), ("k", k), ("v", v)):
+        _check_tensor(name, t, (B, H, N, D), dt, dev)
+    if y is None:
+        y = torch.empty((B, H, N, D), dtype=dt, device=dev)
+    saved = _saved_buffer(B, H, N, M, D, dev)
+    code = dtype_code(k)
+    ws = _workspace(lib.flarepp_workspace_size(B, H, N, M, D, code), dev, workspace)
+    _call(lib.simplified_flarepp_mixer_fwd_train, "simplified_flarepp_mixer_fwd_train", B, H, N,
+          M, D, code, _ptr(q0), _ptr(k0), _ptr(v0), _ptr(k), _ptr(v), _ptr(y), _ptr(saved),
+          saved.numel() * 4, _ptr(ws), ws.numel(), _stream(stream))
+    return y, saved
+
+
+def simplified_flarepp_mixer_bwd(q0, k0, v0, k, v, y, dy, saved, workspace=None, stream=None):
+    """Gradients of the simplified mixer (fp32): dict(dq0, dk0, dv0, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q0.shape[1]
+    dev, dt = k.device, k.dtype
+    _check_tensor("q0", q0, (H, M, D), dt, dev)
+    for name, t in (("k0", k0), ("v0", v0), ("k", k), ("v", v), ("y", y), ("dy", dy)):
+        _check_tensor(name, t, (B, H, N, D), dt, dev)
+    f = dict(device=dev, dtype=torch.float32)
+    g = dict(dq0=torch.empty((H, M, D), **f), dk0=torch.empty((B, H, N, D), **f),
+             dv0=torch.empty((B, H, N, D), **f), dk=torch.empty((B, H, N, D), **f),
+             dv=torch.empty((B, H, N, D), **f))
+    code = dtype_code(k)
+    nbytes = lib.flarepp_bwd_workspace_size(B, H, N, M, D, code)
+    if nbytes == 0:
+        raise FlareppError(FLAREPP_ERR_UNSUPPORTED, "flarepp_bwd_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    _call(lib.simplified_flarepp_mixer_bwd, "simplified_flarepp_mixer_bwd", B, H, N, M, D, code,
+          _ptr(q0), _ptr(k0), _ptr(v0), _ptr(k), _ptr(v), _ptr(y), _ptr(dy), _ptr(saved),
+          saved.numel() * 4, _ptr(g["dq0"]), _ptr(g["dk0"]), _ptr(g["dv0"]), _ptr(g["dk"]),
+          _ptr(g["dv"]), _ptr(ws), ws.numel(), _stream(stream))
     return g

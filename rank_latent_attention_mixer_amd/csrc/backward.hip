@@ -496,17 +496,43 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One wave per token row: -Delta2 = -(dy . y).
+// Dot product of two 16-byte chunks of 8 operand values.
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, int dtype) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const unsigned ua = (a[j] >> (16 * half)) & 0xFFFFu, ub = (b[j] >> (16 * half)) & 0xFFFFu;
+      float fa, fb;
+      if (dtype == kBF16) {
+        fa = __uint_as_float(ua << 16);
+        fb = __uint_as_float(ub << 16);
+      } else {
+        fa = (float)__builtin_bit_cast(_Float16, (unsigned short)ua);
+        fb = (float)__builtin_bit_cast(_Float16, (unsigned short)ub);
+      }
+      acc = fmaf(fa, fb, acc);
+    }
+  return acc;
+}
+
+// -Delta2 = -(dy . y) per token row: D/8 lanes per row, one 16-byte chunk
+// each, reduced over the row's lanes.
 __global__ __launch_bounds__(256) void bwd_tok_prep_kernel(BwdPrepParams a) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int d = threadIdx.x & 63;
-  if (row >= a.rows) return;
-  const bool live = d < a.D;
-  const int64_t i = row * a.D + d;
-  const float dy = live ? ld_any(a.dy, i, a.dtype) : 0.f;
-  const float yv = live ? ld_any(a.y, i, a.dtype) : 0.f;
-  const float delta = wave_sum(dy * yv);
-  if (d == 0) a.negd[row] = -delta;
+  const int cpr = a.D / 8;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = t / cpr;
+  const int c = (int)(t - row * cpr);
+  const bool live = row < a.rows;
+  float v = 0.f;
+  if (live) {
+    const int64_t off = (row * a.D + 8 * c) * 2;
+    v = dot8(ldg16(reinterpret_cast<const unsigned char*>(a.dy) + off),
+             ldg16(reinterpret_cast<const unsigned char*>(a.y) + off), a.dtype);
+  }
+  for (int o = 1; o < cpr; o <<= 1) v += __shfl_xor(v, o);
+  if (live && c == 0) a.negd[row] = -v;
 }
 
 // Latent rows: convert fp32 [sets][M][D] to operand rows [sets][Mpad][D]
@@ -564,7 +590,7 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(BwdGateParams a) {
   for (int md = tid; md < a.M * a.D; md += 256) {
     float acc = 0.f;
     for (int b = 0; b < a.B; ++b) acc += a.dq[((int64_t)(b * a.H + hd) * a.M) * a.D + md];
-    a.dqf[(int64_t)hd * a.M * a.D + md] = acc;
+    if (a.dqf) a.dqf[(int64_t)hd * a.M * a.D + md] = acc;
   }
   if (!a.synthesis) return;
   float part = 0.f;
@@ -585,9 +611,13 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(BwdGateParams a) {
   }
 }
 
-// Normalised latent gradient operand of one set (one workgroup per set).
+// Normalised latent gradient operand: workgroup (set, rb) finds the set's
+// maximum (each of the set's workgroups reads it all, from L2) and writes
+// the rows [16 rb, 16 rb + 16).
+constexpr int kNormRows = 16;
 __global__ __launch_bounds__(256) void bwd_norm_kernel(BwdNormParams a) {
   const int set = blockIdx.x;
+  const int m0 = blockIdx.y * kNormRows;
   const int tid = threadIdx.x;
   const float alpha = a.gate ? gate_sigma(a.gate[set % a.H]) : 1.f;
   const float* src = a.src + (int64_t)set * a.M * a.D;
@@ -604,9 +634,9 @@ __global__ __launch_bounds__(256) void bwd_norm_kernel(BwdNormParams a) {
   // rho = 2^k with max|g| <= rho < 2 max|g| (1 when g = 0)
   const int k = red[0] > 0.f ? (int)ceilf(log2f(red[0])) : 0;
   const float down = exp2f((float)-k);
-  if (tid == 0) a.set_e[set] = (float)k - a.shift;
+  if (tid == 0 && blockIdx.y == 0) a.set_e[set] = (float)k - a.shift;
   const int wv = tid >> 6, d = tid & 63;
-  for (int m = wv; m < a.M; m += 4) {  // one wave per latent row
+  for (int m = m0 + wv; m < min(a.M, m0 + kNormRows); m += 4) {  // one wave per latent row
     const bool live = d < a.D;
     const float g = live ? alpha * src[(int64_t)m * a.D + d] : 0.f;
     const float delta = wave_sum(g * (live ? w[(int64_t)m * a.D + d] : 0.f));
@@ -683,7 +713,8 @@ hipError_t launch_bwd_tok(int dtype, int mode, int D, const BwdTokParams& p, hip
 }
 
 hipError_t launch_bwd_tok_prep(const BwdPrepParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_tok_prep_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, s, p);
+  const int64_t n = p.rows * (p.D / 8);
+  hipLaunchKernelGGL(bwd_tok_prep_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 hipError_t launch_bwd_rows(const BwdRowsParams& p, hipStream_t s) {
@@ -697,7 +728,8 @@ hipError_t launch_bwd_dec_sums(const BwdSumsParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_bwd_norm(const BwdNormParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_norm_kernel, dim3((unsigned)p.sets), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_norm_kernel, dim3((unsigned)p.sets, (unsigned)((p.M + kNormRows - 1) / kNormRows)),
+                     dim3(256), 0, s, p);
   return hipGetLastError();
 }
 hipError_t launch_bwd_add_sums(const BwdAddParams& p, hipStream_t s) {

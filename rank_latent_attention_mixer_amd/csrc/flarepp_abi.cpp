@@ -402,17 +402,23 @@ int make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dty
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Shared by FLARE++ (q0 non-null: synthesis and gate) and FLARE (q0 null,
-// q given, caller scale).
+// Shared by FLARE++ (q0 non-null, v0 == k0: synthesis and gate), the
+// simplified mixer (q0 non-null, v0 its own tensor, no gate: q = q_dyn) and
+// FLARE (q0 null, q given, caller scale).
 int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, float scale,
-             const void* q0, const float* gate, const void* k0, const void* q_flare,
-             const void* k, const void* v, const void* y, const void* dy, const float* saved,
-             size_t saved_bytes, float* dq0, float* dq_lat, float* dgate, float* dk0, float* dk,
-             float* dv, void* ws, size_t ws_bytes, void* stream) {
+             const void* q0, const float* gate, const void* k0, const void* v0,
+             const void* q_flare, const void* k, const void* v, const void* y, const void* dy,
+             const float* saved, size_t saved_bytes, float* dq0, float* dq_lat, float* dgate,
+             float* dk0, float* dv0, float* dk, float* dv, void* ws, size_t ws_bytes,
+             void* stream) {
   const bool pp = q0 != nullptr;
-  if (!k || !v || !y || !dy || !saved || !dq_lat || !dk || !dv) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (pp && (!gate || !k0 || !dq0 || !dgate || !dk0)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (!pp && !q_flare) return FLAREPP_ERR_INVALID_ARGUMENT;
+  const bool simplified = pp && v0 != k0;
+  if (!k || !v || !y || !dy || !saved || !dk || !dv) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (pp && (!k0 || !v0 || !dq0 || !dk0)) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (pp && !simplified && (!gate || !dgate || !dq_lat)) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (simplified && !dv0) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (!pp && (!q_flare || !dq_lat)) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (simplified) gate = nullptr;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FLAREPP_ERR_INVALID_ARGUMENT;
   BwdPlan p;
   int st = make_bwd_plan(B, H, N, M, D, dtype, &p);
@@ -420,19 +426,21 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   Saved sv = saved_layout(B, H, N, M, D, const_cast<float*>(saved));
   if (saved_bytes < sv.floats * sizeof(float) || !aligned16(saved)) return FLAREPP_ERR_WORKSPACE;
   for (const void* g : {(const void*)dq_lat, (const void*)dk, (const void*)dv,
-                        pp ? (const void*)dq0 : nullptr, pp ? (const void*)dk0 : nullptr})
+                        pp ? (const void*)dq0 : nullptr, pp ? (const void*)dk0 : nullptr,
+                        simplified ? (const void*)dv0 : nullptr})
     if (g && !aligned16(g)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  for (const void* in : {k, v, y, dy, pp ? k0 : nullptr})
+  for (const void* in : {k, v, y, dy, pp ? k0 : nullptr, pp ? v0 : nullptr})
     if (in && !aligned16(in)) return FLAREPP_ERR_INVALID_ARGUMENT;
   const size_t tokf = (size_t)(B * H * N * D) * 4, latf = (size_t)(H * M * D) * 4;
   const size_t toke = (size_t)(B * H * N * D) * 2;
-  for (const void* g : {(const void*)dk, (const void*)dv, pp ? (const void*)dk0 : nullptr}) {
+  for (const void* g : {(const void*)dk, (const void*)dv, pp ? (const void*)dk0 : nullptr,
+                        simplified ? (const void*)dv0 : nullptr}) {
     if (!g) continue;
-    for (const void* in : {k, v, y, dy, pp ? k0 : nullptr})
+    for (const void* in : {k, v, y, dy, pp ? k0 : nullptr, pp ? v0 : nullptr})
       if (in && overlaps(g, tokf, in, toke)) return FLAREPP_ERR_INVALID_ARGUMENT;
     if (overlaps(g, tokf, saved, sv.floats * 4)) return FLAREPP_ERR_INVALID_ARGUMENT;
   }
-  if (overlaps(dq_lat, latf, saved, sv.floats * 4)) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (dq_lat && overlaps(dq_lat, latf, saved, sv.floats * 4)) return FLAREPP_ERR_INVALID_ARGUMENT;
   if (ws == nullptr || ws_bytes < p.total || ((uintptr_t)ws % kAlign) != 0)
     return FLAREPP_ERR_WORKSPACE;
   if ((st = check_device()) != FLAREPP_OK) return st;
@@ -522,11 +530,12 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   std::memset(&gp, 0, sizeof(gp));
   gp.H = (int)H; gp.B = (int)B; gp.M = (int)M; gp.Mpad = p.Mpad; gp.D = (int)D;
   gp.gate = gate; gp.dq = f32(p.off_dq); gp.qd = sv.qd; gp.dqf = dq_lat; gp.dgate = dgate;
-  gp.synthesis = pp ? 1 : 0;
-  FLAREPP_TRY(launch_bwd_gate(gp, s));
+  gp.synthesis = pp && !simplified ? 1 : 0;
+  if (!simplified) FLAREPP_TRY(launch_bwd_gate(gp, s));
   if (!pp) return FLAREPP_OK;
 
-  // dqd' rows and -Delta0 = -(dqd . q_dyn), dqd = sigma dq, normalised per set
+  // dqd' rows and -Delta0 = -(dqd . q_dyn), dqd = sigma dq (simplified:
+  // sigma = 1), normalised per set
   np.src = f32(p.off_dq); np.w = sv.qd; np.gate = gate; np.rows = at(p.off_dqdp);
   np.negd = f32(p.off_nd0); np.set_e = f32(p.off_e0);
   FLAREPP_TRY(launch_bwd_norm(np, s));
@@ -539,22 +548,24 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   // dq0 = s dS0 k0 per (b, h), then summed over the batch
   lp.qop = at(p.off_cq0); lp.q_b_stride = 0; lp.q_h_stride = rowH;
   lp.gop = at(p.off_dqdp); lp.lse = sv.lse0; lp.negg = f32(p.off_nd0);
-  lp.t[0] = k0; lp.t[1] = nullptr;
+  lp.t[0] = k0; lp.t[1] = simplified ? v0 : nullptr;
   lp.gate = gate;
-  FLAREPP_TRY(launch_bwd_lat(dtype, kBwdLatSyn, (int)D, lp, s));
+  // with values k0 the G rows are the score rows (one token tensor)
+  FLAREPP_TRY(launch_bwd_lat(dtype, simplified ? kBwdLatEnc : kBwdLatSyn, (int)D, lp, s));
   ap.dst = f32(p.off_dq0s); ap.accumulate = 0; ap.set_e = f32(p.off_e0);
   FLAREPP_TRY(launch_bwd_add_sums(ap, s));
   BwdGateParams g0 = gp;
   g0.dq = f32(p.off_dq0s); g0.dqf = dq0; g0.dgate = nullptr; g0.synthesis = 0;
   FLAREPP_TRY(launch_bwd_gate(g0, s));
-  // dk0 = A0^T dqd + s dS0^T q0 (k0 is key and value of the synthesis)
+  // dk0 = s dS0^T q0 and dv0 = A0^T dqd (FLARE++: k0 is key and value, the
+  // two are summed)
   BwdTokParams k0p;
   std::memset(&k0p, 0, sizeof(k0p));
   k0p.lat[0] = at(p.off_cq0); k0p.lat_b_stride[0] = 0; k0p.lat_h_stride[0] = rowH;
   k0p.lat[2] = at(p.off_dqdp); k0p.lat_b_stride[2] = H * rowH; k0p.lat_h_stride[2] = rowH;
   k0p.lat_lse = sv.lse0; k0p.lat_negd = f32(p.off_nd0);
-  k0p.kt = k0; k0p.g2t = k0;
-  k0p.out0 = dk0; k0p.out1 = nullptr; k0p.s_over_c = scale / c; k0p.shift = shift;
+  k0p.kt = k0; k0p.g2t = v0;
+  k0p.out0 = dk0; k0p.out1 = simplified ? dv0 : nullptr; k0p.s_over_c = scale / c; k0p.shift = shift;
   k0p.set_e = f32(p.off_e0);
   k0p.gate = gate;
   k0p.B = (int)B; k0p.H = (int)H; k0p.N = N; k0p.M = (int)M; k0p.wg_per_bh = p.tok_wg_per_bh;
@@ -767,9 +778,10 @@ int flarepp_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int
                       size_t workspace_bytes, void* stream) {
   try {
     if (!q0 || !q_fixed) return FLAREPP_ERR_INVALID_ARGUMENT;
+    if (!gate) return FLAREPP_ERR_INVALID_ARGUMENT;
     return bwd_impl(B, H, N, M, D, dtype, (float)(1.0 / std::sqrt((double)D)), q0, gate, k0,
-                    nullptr, k, v, y, dy, saved, saved_bytes, dq0, dq_fixed, dgate, dk0, dk, dv,
-                    workspace, workspace_bytes, stream);
+                    k0, nullptr, k, v, y, dy, saved, saved_bytes, dq0, dq_fixed, dgate, dk0,
+                    nullptr, dk, dv, workspace, workspace_bytes, stream);
   } catch (...) {
     return FLAREPP_ERR_HIP;
   }
@@ -781,9 +793,40 @@ int flare_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int d
                     float* dv, void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (!q) return FLAREPP_ERR_INVALID_ARGUMENT;
-    return bwd_impl(B, H, N, M, D, dtype, scale, nullptr, nullptr, nullptr, q, k, v, y, dy,
-                    saved, saved_bytes, nullptr, dq, nullptr, nullptr, dk, dv, workspace,
-                    workspace_bytes, stream);
+    return bwd_impl(B, H, N, M, D, dtype, scale, nullptr, nullptr, nullptr, nullptr, q, k, v, y,
+                    dy, saved, saved_bytes, nullptr, dq, nullptr, nullptr, nullptr, dk, dv,
+                    workspace, workspace_bytes, stream);
+  } catch (...) {
+    return FLAREPP_ERR_HIP;
+  }
+}
+
+int simplified_flarepp_mixer_fwd_train(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                       int dtype, const void* q0, const void* k0, const void* v0,
+                                       const void* k, const void* v, void* y, float* saved,
+                                       size_t saved_bytes, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  try {
+    if (!saved) return FLAREPP_ERR_INVALID_ARGUMENT;
+    return mixer_impl(B, H, N, M, D, dtype, q0, nullptr, nullptr, k0, v0, k, v, y, workspace,
+                      workspace_bytes, stream, nullptr, saved, saved_bytes);
+  } catch (...) {
+    return FLAREPP_ERR_HIP;
+  }
+}
+
+int simplified_flarepp_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                                 int dtype, const void* q0, const void* k0, const void* v0,
+                                 const void* k, const void* v, const void* y, const void* dy,
+                                 const float* saved, size_t saved_bytes, float* dq0, float* dk0,
+                                 float* dv0, float* dk, float* dv, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  try {
+    if (!q0 || !k0 || !v0) return FLAREPP_ERR_INVALID_ARGUMENT;
+    if (k0 == v0) return FLAREPP_ERR_INVALID_ARGUMENT;  // the FLARE++ entry point covers v0 == k0
+    return bwd_impl(B, H, N, M, D, dtype, (float)(1.0 / std::sqrt((double)D)), q0, nullptr, k0,
+                    v0, nullptr, k, v, y, dy, saved, saved_bytes, dq0, nullptr, nullptr, dk0,
+                    dv0, dk, dv, workspace, workspace_bytes, stream);
   } catch (...) {
     return FLAREPP_ERR_HIP;
   }

@@ -238,3 +238,24 @@ def test_fwd_train_rejects_small_saved_buffer():
                                      ws, None) == WS
     assert L.flare_mixer_fwd_train(B, H, N, M, D, dt, 0.5, FAKE["q0"], FAKE["k"], FAKE["v"],
                                    FAKE["y"], GRADS["saved"], 64, FAKE["ws"], ws, None) == WS
+
+
+def test_simplified_bwd_validates():
+    B, H, N, M, D, dt = 1, 2, 1024, 16, 32, 1
+    L = lib()
+    sb = L.flarepp_saved_size(B, H, N, M, D)
+    wsb = L.flarepp_bwd_workspace_size(B, H, N, M, D, dt)
+    P = lambda n: FAKE.get(n) or GRADS[n]
+
+    def call(v0="v0", dv0="dv", dk0="dk0", dk="dq0"):
+        return L.simplified_flarepp_mixer_bwd(
+            B, H, N, M, D, dt, P("q0"), P("k0"), None if v0 is None else P(v0), P("k"), P("v"),
+            P("y"), P("dy"), P("saved"), sb, P("dqf"), P(dk0),
+            None if dv0 is None else P(dv0), P(dk), P("dgate"), P("bws"), wsb, None)
+    assert call(v0="k0") == INV          # v0 == k0 belongs to flarepp_mixer_bwd
+    assert call(v0=None) == INV
+    assert call(dv0=None) == INV
+    assert call(dv0="v0") == INV         # gradient overlaps an input
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == HIP

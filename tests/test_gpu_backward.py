@@ -204,6 +204,24 @@ def test_workload_bwd(fp, name, heads):
     check_flarepp(name, got, ref, w.dtype, heads=heads)
 
 
+@pytest.mark.timeout(600)
+def test_million_token_bwd_sampled_head(fp):
+    """The million-token workload at full size (the launch shapes the
+    backward bench times); the oracle checks head 0 whole (about 40 s of
+    fp64 CPU work)."""
+    name = "million_token_bf16"
+    w = WORKLOADS[name]
+    note(f"[bwd] workload {name} {w.shape_dict}")
+    x = make_inputs(name)
+    dy = make_cotangent(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed + 100)
+    got, _ = run_flarepp_bwd(fp, x, dy, w.dtype)
+    for n, g in got.items():
+        assert np.all(np.isfinite(g)), n
+    xs, dys = _head_slice(x, dy, [0])
+    ref = oracle.flarepp_bwd_ref(**f64(xs), dy=np.asarray(dys, np.float64))
+    check_flarepp(name, got, ref, w.dtype, heads=[0])
+
+
 def test_bwd_deterministic(fp):
     """Fixed reduction orders: two runs give identical gradients."""
     x = make_random_inputs(2, 2, 3000, 96, 32, "bf16", seed=12)
@@ -222,3 +240,30 @@ def test_fwd_train_output_equals_forward(fp):
     y1, _ = fp.flarepp_mixer_fwd_train(d["q0"], d["q_fixed"], d["gate"], d["k0"], d["k"], d["v"])
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("B,H,N,M,D,dtype", [
+    (2, 2, 700, 80, 32, "bf16"),
+    (1, 2, 1000, 64, 16, "fp16"),
+    (1, 1, 513, 100, 64, "bf16"),
+    (2, 1, 300, 33, 64, "fp16"),
+])
+def test_simplified_bwd_vs_oracle(fp, B, H, N, M, D, dtype):
+    """Simplified mixer (separate synthesis values, q = q_dyn) against
+    oracle.simplified_flarepp_bwd_ref."""
+    from flarepp_workloads import make_simplified_inputs
+    note(f"[bwd] simplified B={B} H={H} N={N} M={M} D={D} {dtype}")
+    x = make_simplified_inputs(B, H, N, M, D, dtype, seed=40 + N)
+    dy = make_cotangent(B, H, N, D, dtype, seed=41 + N)
+    d = {n: dev(x[n], dtype) for n in ("q0", "k0", "v0", "k", "v")}
+    y, saved = fp.simplified_flarepp_mixer_fwd_train(d["q0"], d["k0"], d["v0"], d["k"], d["v"])
+    g = fp.simplified_flarepp_mixer_bwd(d["q0"], d["k0"], d["v0"], d["k"], d["v"], y,
+                                        dev(dy, dtype), saved)
+    torch.cuda.synchronize()
+    ref = oracle.simplified_flarepp_bwd_ref(
+        **{n: np.asarray(x[n], np.float64) for n in ("q0", "k0", "v0", "k", "v")},
+        dy=np.asarray(dy, np.float64))
+    errs = {n: rel_err(g[n].cpu().numpy(), ref[n]) for n in ("dq0", "dk0", "dv0", "dk", "dv")}
+    note("[bwd] simplified " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[dtype], (n, e)
