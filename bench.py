@@ -69,9 +69,13 @@ class HipEvents:
 
 
 def source_digest() -> str:
+    """Digest of the forward's sources (kernels, shared headers, the forward
+    launch plan); the backward's own files are left out."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_latent_attention_mixer_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f.startswith("backward"):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

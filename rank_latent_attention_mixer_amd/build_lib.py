@@ -22,7 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflarepp.so")
 
-SOURCES = ["encode_split.hip", "combine.hip", "decode.hip", "backward.hip", "flarepp_abi.cpp"]
+SOURCES = ["encode_split.hip", "combine.hip", "decode.hip", "backward.hip", "flarepp_abi.cpp",
+           "backward_abi.cpp"]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

@@ -34,8 +34,8 @@
 // keys with P or T as the B operand.
 #include <cmath>
 
+#include "backward.hpp"
 #include "flash_tile.hpp"
-#include "kernels.hpp"
 
 namespace flarepp {
 

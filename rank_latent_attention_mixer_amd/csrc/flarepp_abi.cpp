@@ -10,7 +10,30 @@
 #include <cmath>
 #include <cstring>
 
+#include "abi_common.hpp"
 #include "kernels.hpp"
+
+namespace flarepp {
+
+// gfx950 check for the current device, cached per device id.
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLAREPP_ERR_HIP;
+  if (dev < 64) {
+    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return FLAREPP_OK;
+    if (c == 2) return FLAREPP_ERR_UNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FLAREPP_ERR_HIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FLAREPP_OK : FLAREPP_ERR_UNSUPPORTED;
+}
+
+}  // namespace flarepp
 
 namespace {
 
@@ -18,13 +41,6 @@ using namespace flarepp;
 
 constexpr int kEncTile = 64;        // granularity of caller-chosen encoder chunks
 constexpr int kEncTargetWgs = 512;  // encoder workgroups aimed for (2 per CU)
-constexpr int kDecTargetWgs = 256;   // persistent decoder workgroups (one per CU)
-constexpr size_t kAlign = 256;
-
-size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
-
-int esize_of(int dtype) { return dtype == FLAREPP_F32 ? 4 : 2; }
-
 struct Plan {
   int64_t B, H, N, M, D;
   int dtype;
@@ -34,25 +50,6 @@ struct Plan {
   int dec_wg_per_bh;
   size_t off_pm, off_pl, off_po, off_q0, off_q, off_z, total;
 };
-
-bool mul_ok(int64_t a, int64_t b, int64_t* out) {
-  return !__builtin_mul_overflow(a, b, out);
-}
-
-// Shape checks shared by every entry point (no HIP call).
-int check_shape(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype) {
-  if (B < 1 || H < 1 || N < 1 || M < 1 || D < 1) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (dtype != FLAREPP_F32 && dtype != FLAREPP_BF16 && dtype != FLAREPP_F16)
-    return FLAREPP_ERR_INVALID_ARGUMENT;
-  int64_t t;
-  if (!mul_ok(B, H, &t) || !mul_ok(t, N, &t) || !mul_ok(t, D, &t) || !mul_ok(t, 4, &t))
-    return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (!mul_ok(H, M, &t) || !mul_ok(t, D, &t)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (B * H > (int64_t)1 << 24) return FLAREPP_ERR_INVALID_ARGUMENT;  // grid limits
-  if (D != 8 && D != 16 && D != 32 && D != 64) return FLAREPP_ERR_UNSUPPORTED;
-  if (M > FLAREPP_MAX_M) return FLAREPP_ERR_UNSUPPORTED;
-  return FLAREPP_OK;
-}
 
 int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
               int64_t chunk_tokens, Plan* p) {
@@ -100,38 +97,11 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   return FLAREPP_OK;
 }
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
-}
-
 int check_workspace(const Plan& p, void* ws, size_t bytes) {
   if (ws == nullptr || bytes < p.total || ((uintptr_t)ws % kAlign) != 0)
     return FLAREPP_ERR_WORKSPACE;
   return FLAREPP_OK;
 }
-
-// gfx950 check for the current device, cached per device id.
-std::atomic<int> g_arch_ok[64];
-
-int check_device() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLAREPP_ERR_HIP;
-  if (dev < 64) {
-    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
-    if (c == 1) return FLAREPP_OK;
-    if (c == 2) return FLAREPP_ERR_UNSUPPORTED;
-  }
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FLAREPP_ERR_HIP;
-  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
-  return ok ? FLAREPP_OK : FLAREPP_ERR_UNSUPPORTED;
-}
-
-int hip_status(hipError_t e) { return e == hipSuccess ? FLAREPP_OK : FLAREPP_ERR_HIP; }
-
-unsigned char* ws_at(void* ws, size_t off) { return static_cast<unsigned char*>(ws) + off; }
 
 EncodeParams encode_params(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh,
                            const void* k, const void* v, const float* gate) {
@@ -151,24 +121,6 @@ EncodeParams encode_params(const Plan& p, void* ws, const void* q, int64_t qb, i
 // layouts): q [B,H,M,D] (the routing query), z [B,H,M,D], q_dyn [B,H,M,D],
 // base-2 log-sum-exp of the synthesis and encoder rows [B,H,M] and of the
 // decoder rows [B,H,N].
-struct Saved {
-  float *q, *z, *qd, *lse0, *lse1, *lse2;
-  size_t floats;
-};
-Saved saved_layout(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, float* base) {
-  Saved v;
-  const size_t lat = (size_t)(B * H * M * D), row = (size_t)(B * H * M);
-  size_t o = 0;
-  v.q = base + o; o += lat;
-  v.z = base + o; o += lat;
-  v.qd = base + o; o += lat;
-  v.lse0 = base + o; o += row;
-  v.lse1 = base + o; o += row;
-  v.lse2 = base + o; o += (size_t)(B * H * N);
-  v.floats = o;
-  return v;
-}
-
 CombineParams combine_base(const Plan& p, void* ws) {
   CombineParams c;
   std::memset(&c, 0, sizeof(c));
@@ -222,12 +174,6 @@ hipError_t decode(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh
   d.wg_per_bh = p.dec_wg_per_bh;
   return launch_decode(p.dtype, (int)p.D, d, s);
 }
-
-#define FLAREPP_TRY(expr)                        \
-  do {                                           \
-    const hipError_t e_ = (expr);                \
-    if (e_ != hipSuccess) return FLAREPP_ERR_HIP; \
-  } while (0)
 
 // FLARE++ (v0 == k0, q_fixed and gate given) and simplified FLARE++ (own
 // synthesis values v0, q_fixed == gate == NULL: q is the synthesized query).
@@ -338,240 +284,6 @@ int flare_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   return FLAREPP_OK;
 }
 
-
-// ---------------------------------------------------------------------------
-// Backward pass
-// ---------------------------------------------------------------------------
-
-constexpr int kBwdTargetWgs = 512;
-
-struct BwdPlan {
-  int64_t B, H, N, M, D;
-  int dtype, Mpad, nchunks, mblocks, tok_wg_per_bh;
-  int64_t chunk_tokens;
-  size_t off_cq, off_zr, off_nd2, off_py, off_px, off_dq, off_dz, off_dzp, off_nd1, off_e1,
-      off_cq0, off_dqdp, off_nd0, off_e0, off_dq0s, total;
-};
-
-int make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, BwdPlan* p) {
-  int st = check_shape(B, H, N, M, D, dtype);
-  if (st != FLAREPP_OK) return st;
-  if (dtype == FLAREPP_F32 || D < 16) return FLAREPP_ERR_UNSUPPORTED;  // matrix-core path only
-  if (bwd_tok_lds_bytes((int)M, (int)D) > 160 * 1024) return FLAREPP_ERR_UNSUPPORTED;
-  p->B = B; p->H = H; p->N = N; p->M = M; p->D = D; p->dtype = dtype;
-  p->Mpad = (int)((M + 31) / 32 * 32);
-  const int64_t BH = B * H;
-  p->mblocks = (int)((M + bwd_latents_per_block() - 1) / bwd_latents_per_block());
-  const int64_t unit = 128;
-  const int64_t tiles = (N + unit - 1) / unit;
-  int64_t c = (kBwdTargetWgs + BH * p->mblocks - 1) / (BH * p->mblocks);
-  if (c < 1) c = 1;
-  if (c > tiles) c = tiles;
-  p->chunk_tokens = (tiles + c - 1) / c * unit;
-  p->nchunks = (int)((N + p->chunk_tokens - 1) / p->chunk_tokens);
-  int64_t w = (kDecTargetWgs + BH - 1) / BH;
-  const int64_t ttiles = (N + bwd_tokens_per_tile() - 1) / bwd_tokens_per_tile();
-  if (w > ttiles) w = ttiles;
-  if (w < 1) w = 1;
-  p->tok_wg_per_bh = (int)w;
-  int64_t wgs;
-  if (!mul_ok(BH * p->mblocks, p->nchunks, &wgs) || wgs > 0x7FFFFFFF) return FLAREPP_ERR_INVALID_ARGUMENT;
-  const size_t es = 2, f = 4;
-  const size_t rows = (size_t)BH * p->Mpad * D;
-  const size_t part = (size_t)BH * p->nchunks * p->Mpad * D * f;
-  size_t off = 0;
-  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
-  p->off_cq = take(rows * es);
-  p->off_zr = take(rows * es);
-  p->off_nd2 = take((size_t)BH * N * f);
-  p->off_py = take(part);
-  p->off_px = take(part);
-  p->off_dq = take((size_t)BH * M * D * f);
-  p->off_dz = take((size_t)BH * M * D * f);
-  p->off_dzp = take(rows * es);
-  p->off_nd1 = take((size_t)BH * M * f);
-  p->off_e1 = take((size_t)BH * f);
-  p->off_cq0 = take((size_t)H * p->Mpad * D * es);
-  p->off_dqdp = take(rows * es);
-  p->off_nd0 = take((size_t)BH * M * f);
-  p->off_e0 = take((size_t)BH * f);
-  p->off_dq0s = take((size_t)BH * M * D * f);
-  p->total = off;
-  return FLAREPP_OK;
-}
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-
-// Shared by FLARE++ (q0 non-null, v0 == k0: synthesis and gate), the
-// simplified mixer (q0 non-null, v0 its own tensor, no gate: q = q_dyn) and
-// FLARE (q0 null, q given, caller scale).
-int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, float scale,
-             const void* q0, const float* gate, const void* k0, const void* v0,
-             const void* q_flare, const void* k, const void* v, const void* y, const void* dy,
-             const float* saved, size_t saved_bytes, float* dq0, float* dq_lat, float* dgate,
-             float* dk0, float* dv0, float* dk, float* dv, void* ws, size_t ws_bytes,
-             void* stream) {
-  const bool pp = q0 != nullptr;
-  const bool simplified = pp && v0 != k0;
-  if (!k || !v || !y || !dy || !saved || !dk || !dv) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (pp && (!k0 || !v0 || !dq0 || !dk0)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (pp && !simplified && (!gate || !dgate || !dq_lat)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (simplified && !dv0) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (!pp && (!q_flare || !dq_lat)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (simplified) gate = nullptr;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  BwdPlan p;
-  int st = make_bwd_plan(B, H, N, M, D, dtype, &p);
-  if (st != FLAREPP_OK) return st;
-  Saved sv = saved_layout(B, H, N, M, D, const_cast<float*>(saved));
-  if (saved_bytes < sv.floats * sizeof(float) || !aligned16(saved)) return FLAREPP_ERR_WORKSPACE;
-  for (const void* g : {(const void*)dq_lat, (const void*)dk, (const void*)dv,
-                        pp ? (const void*)dq0 : nullptr, pp ? (const void*)dk0 : nullptr,
-                        simplified ? (const void*)dv0 : nullptr})
-    if (g && !aligned16(g)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  for (const void* in : {k, v, y, dy, pp ? k0 : nullptr, pp ? v0 : nullptr})
-    if (in && !aligned16(in)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  const size_t tokf = (size_t)(B * H * N * D) * 4, latf = (size_t)(H * M * D) * 4;
-  const size_t toke = (size_t)(B * H * N * D) * 2;
-  for (const void* g : {(const void*)dk, (const void*)dv, pp ? (const void*)dk0 : nullptr,
-                        simplified ? (const void*)dv0 : nullptr}) {
-    if (!g) continue;
-    for (const void* in : {k, v, y, dy, pp ? k0 : nullptr, pp ? v0 : nullptr})
-      if (in && overlaps(g, tokf, in, toke)) return FLAREPP_ERR_INVALID_ARGUMENT;
-    if (overlaps(g, tokf, saved, sv.floats * 4)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  }
-  if (dq_lat && overlaps(dq_lat, latf, saved, sv.floats * 4)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  if (ws == nullptr || ws_bytes < p.total || ((uintptr_t)ws % kAlign) != 0)
-    return FLAREPP_ERR_WORKSPACE;
-  if ((st = check_device()) != FLAREPP_OK) return st;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // the forward's score factor, bit for bit (it rounds c q to the operand type)
-  const float c = pp ? (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634)
-                     : (float)((double)scale * 1.4426950408889634);
-  // weights normalised over the N tokens are taken times 2^shift so that
-  // ~1/N stays a normal fp16 number while P times a gradient term stays
-  // far below the fp16 maximum
-  const float shift = (float)std::min(8.0, std::max(0.0, std::floor(std::log2((double)N)) - 8.0));
-  const int64_t BH = B * H;
-  const int64_t rowH = (int64_t)p.Mpad * D;   // elements per latent set of operand rows
-  auto at = [&](size_t off) { return ws_at(ws, off); };
-  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws_at(ws, off)); };
-
-  // operand rows of the saved routing query (scaled) and z
-  BwdRowsParams rp;
-  rp.dtype = dtype; rp.M = (int)M; rp.Mpad = p.Mpad; rp.D = (int)D;
-  if (pp) {
-    rp.in = sv.q; rp.in_dtype = FLAREPP_F32; rp.in_sets = (int)BH; rp.in_set_stride = M * D;
-  } else {
-    rp.in = q_flare; rp.in_dtype = dtype; rp.in_sets = (int)H; rp.in_set_stride = M * D;
-  }
-  rp.sets = (int)BH; rp.out = at(p.off_cq); rp.scale = c;
-  FLAREPP_TRY(launch_bwd_rows(rp, s));
-  rp.in = sv.z; rp.in_dtype = FLAREPP_F32; rp.in_sets = (int)BH; rp.in_set_stride = M * D;
-  rp.out = at(p.off_zr); rp.scale = 1.f;
-  FLAREPP_TRY(launch_bwd_rows(rp, s));
-
-  // -Delta2 per token
-  BwdPrepParams tp;
-  tp.dy = dy; tp.y = y; tp.negd = f32(p.off_nd2);
-  tp.rows = BH * N; tp.D = (int)D; tp.dtype = dtype;
-  FLAREPP_TRY(launch_bwd_tok_prep(tp, s));
-
-  // decoder, sums over tokens: dz = A2^T dy, dq = s dS2^T k
-  BwdLatParams lp;
-  std::memset(&lp, 0, sizeof(lp));
-  lp.qop = at(p.off_cq); lp.q_b_stride = H * rowH; lp.q_h_stride = rowH;
-  lp.gop = at(p.off_zr);
-  lp.tok_lse = sv.lse2; lp.tok_negd = f32(p.off_nd2);
-  lp.t[0] = k; lp.t[1] = dy;
-  lp.part[0] = f32(p.off_py); lp.part[1] = f32(p.off_px);
-  lp.B = (int)B; lp.H = (int)H; lp.N = N; lp.M = (int)M; lp.Mpad = p.Mpad;
-  lp.chunk_tokens = p.chunk_tokens; lp.nchunks = p.nchunks; lp.shift = shift;
-  FLAREPP_TRY(launch_bwd_lat(dtype, kBwdLatDec, (int)D, lp, s));
-  BwdSumsParams sp;
-  sp.part[0] = f32(p.off_py); sp.part[1] = f32(p.off_px);
-  sp.nchunks = p.nchunks; sp.Mpad = p.Mpad; sp.M = (int)M; sp.D = (int)D; sp.sets = (int)BH;
-  sp.dq = f32(p.off_dq); sp.dz = f32(p.off_dz); sp.s = scale;
-  FLAREPP_TRY(launch_bwd_dec_sums(sp, s));
-  // dz' rows and -Delta1 = -(dz . z), normalised per set
-  BwdNormParams np;
-  np.src = f32(p.off_dz); np.w = sv.z; np.gate = nullptr; np.rows = at(p.off_dzp);
-  np.negd = f32(p.off_nd1); np.set_e = f32(p.off_e1);
-  np.H = (int)H; np.M = (int)M; np.Mpad = p.Mpad; np.D = (int)D; np.sets = (int)BH;
-  np.dtype = dtype; np.shift = shift;
-  FLAREPP_TRY(launch_bwd_norm(np, s));
-  // encoder, sums over tokens: dq += s dS1 k
-  lp.gop = at(p.off_dzp);
-  lp.lse = sv.lse1; lp.negg = f32(p.off_nd1);
-  lp.tok_lse = nullptr; lp.tok_negd = nullptr;
-  lp.t[1] = v;
-  FLAREPP_TRY(launch_bwd_lat(dtype, kBwdLatEnc, (int)D, lp, s));
-  BwdAddParams ap;
-  ap.part = f32(p.off_py); ap.nchunks = p.nchunks; ap.Mpad = p.Mpad; ap.M = (int)M;
-  ap.D = (int)D; ap.sets = (int)BH; ap.dst = f32(p.off_dq); ap.s = scale; ap.accumulate = 1;
-  ap.set_e = f32(p.off_e1);
-  FLAREPP_TRY(launch_bwd_add_sums(ap, s));
-  // per token, both attentions: dk = s (dS2 + dS1^T) q, dv = A1^T dz
-  BwdTokParams kp;
-  std::memset(&kp, 0, sizeof(kp));
-  kp.lat[0] = at(p.off_cq); kp.lat[1] = at(p.off_zr); kp.lat[2] = at(p.off_dzp);
-  for (int t = 0; t < 3; ++t) { kp.lat_b_stride[t] = H * rowH; kp.lat_h_stride[t] = rowH; }
-  kp.lat_lse = sv.lse1; kp.lat_negd = f32(p.off_nd1);
-  kp.kt = k; kp.g1t = dy; kp.g2t = v;
-  kp.tok_lse = sv.lse2; kp.tok_negd = f32(p.off_nd2);
-  kp.out0 = dk; kp.out1 = dv; kp.s_over_c = scale / c; kp.shift = shift;
-  kp.set_e = f32(p.off_e1);
-  kp.B = (int)B; kp.H = (int)H; kp.N = N; kp.M = (int)M; kp.wg_per_bh = p.tok_wg_per_bh;
-  FLAREPP_TRY(launch_bwd_tok(dtype, kBwdTokFlare, (int)D, kp, s));
-
-  // latent gradient summed over the batch; FLARE++: gate and synthesis operands
-  BwdGateParams gp;
-  std::memset(&gp, 0, sizeof(gp));
-  gp.H = (int)H; gp.B = (int)B; gp.M = (int)M; gp.Mpad = p.Mpad; gp.D = (int)D;
-  gp.gate = gate; gp.dq = f32(p.off_dq); gp.qd = sv.qd; gp.dqf = dq_lat; gp.dgate = dgate;
-  gp.synthesis = pp && !simplified ? 1 : 0;
-  if (!simplified) FLAREPP_TRY(launch_bwd_gate(gp, s));
-  if (!pp) return FLAREPP_OK;
-
-  // dqd' rows and -Delta0 = -(dqd . q_dyn), dqd = sigma dq (simplified:
-  // sigma = 1), normalised per set
-  np.src = f32(p.off_dq); np.w = sv.qd; np.gate = gate; np.rows = at(p.off_dqdp);
-  np.negd = f32(p.off_nd0); np.set_e = f32(p.off_e0);
-  FLAREPP_TRY(launch_bwd_norm(np, s));
-
-  // synthesis: seeds as operand rows (shared over the batch)
-  BwdRowsParams r0 = rp;
-  r0.in = q0; r0.in_dtype = dtype; r0.in_sets = (int)H; r0.in_set_stride = M * D;
-  r0.sets = (int)H; r0.out = at(p.off_cq0); r0.scale = c;
-  FLAREPP_TRY(launch_bwd_rows(r0, s));
-  // dq0 = s dS0 k0 per (b, h), then summed over the batch
-  lp.qop = at(p.off_cq0); lp.q_b_stride = 0; lp.q_h_stride = rowH;
-  lp.gop = at(p.off_dqdp); lp.lse = sv.lse0; lp.negg = f32(p.off_nd0);
-  lp.t[0] = k0; lp.t[1] = simplified ? v0 : nullptr;
-  lp.gate = gate;
-  // with values k0 the G rows are the score rows (one token tensor)
-  FLAREPP_TRY(launch_bwd_lat(dtype, simplified ? kBwdLatEnc : kBwdLatSyn, (int)D, lp, s));
-  ap.dst = f32(p.off_dq0s); ap.accumulate = 0; ap.set_e = f32(p.off_e0);
-  FLAREPP_TRY(launch_bwd_add_sums(ap, s));
-  BwdGateParams g0 = gp;
-  g0.dq = f32(p.off_dq0s); g0.dqf = dq0; g0.dgate = nullptr; g0.synthesis = 0;
-  FLAREPP_TRY(launch_bwd_gate(g0, s));
-  // dk0 = s dS0^T q0 and dv0 = A0^T dqd (FLARE++: k0 is key and value, the
-  // two are summed)
-  BwdTokParams k0p;
-  std::memset(&k0p, 0, sizeof(k0p));
-  k0p.lat[0] = at(p.off_cq0); k0p.lat_b_stride[0] = 0; k0p.lat_h_stride[0] = rowH;
-  k0p.lat[2] = at(p.off_dqdp); k0p.lat_b_stride[2] = H * rowH; k0p.lat_h_stride[2] = rowH;
-  k0p.lat_lse = sv.lse0; k0p.lat_negd = f32(p.off_nd0);
-  k0p.kt = k0; k0p.g2t = v0;
-  k0p.out0 = dk0; k0p.out1 = simplified ? dv0 : nullptr; k0p.s_over_c = scale / c; k0p.shift = shift;
-  k0p.set_e = f32(p.off_e0);
-  k0p.gate = gate;
-  k0p.B = (int)B; k0p.H = (int)H; k0p.N = N; k0p.M = (int)M; k0p.wg_per_bh = p.tok_wg_per_bh;
-  FLAREPP_TRY(launch_bwd_tok(dtype, kBwdTokSyn, (int)D, k0p, s));
-  return FLAREPP_OK;
-}
 
 }  // namespace
 
@@ -763,44 +475,6 @@ int flare_mixer_fwd_train(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
   }
 }
 
-size_t flarepp_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
-                                  int dtype) {
-  BwdPlan p;
-  if (make_bwd_plan(B, H, N, M, D, dtype, &p) != FLAREPP_OK) return 0;
-  return p.total;
-}
-
-int flarepp_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
-                      const void* q0, const void* q_fixed, const float* gate, const void* k0,
-                      const void* k, const void* v, const void* y, const void* dy,
-                      const float* saved, size_t saved_bytes, float* dq0, float* dq_fixed,
-                      float* dgate, float* dk0, float* dk, float* dv, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  try {
-    if (!q0 || !q_fixed) return FLAREPP_ERR_INVALID_ARGUMENT;
-    if (!gate) return FLAREPP_ERR_INVALID_ARGUMENT;
-    return bwd_impl(B, H, N, M, D, dtype, (float)(1.0 / std::sqrt((double)D)), q0, gate, k0,
-                    k0, nullptr, k, v, y, dy, saved, saved_bytes, dq0, dq_fixed, dgate, dk0,
-                    nullptr, dk, dv, workspace, workspace_bytes, stream);
-  } catch (...) {
-    return FLAREPP_ERR_HIP;
-  }
-}
-
-int flare_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
-                    float scale, const void* q, const void* k, const void* v, const void* y,
-                    const void* dy, const float* saved, size_t saved_bytes, float* dq, float* dk,
-                    float* dv, void* workspace, size_t workspace_bytes, void* stream) {
-  try {
-    if (!q) return FLAREPP_ERR_INVALID_ARGUMENT;
-    return bwd_impl(B, H, N, M, D, dtype, scale, nullptr, nullptr, nullptr, nullptr, q, k, v, y,
-                    dy, saved, saved_bytes, nullptr, dq, nullptr, nullptr, nullptr, dk, dv,
-                    workspace, workspace_bytes, stream);
-  } catch (...) {
-    return FLAREPP_ERR_HIP;
-  }
-}
-
 int simplified_flarepp_mixer_fwd_train(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
                                        int dtype, const void* q0, const void* k0, const void* v0,
                                        const void* k, const void* v, void* y, float* saved,
@@ -810,23 +484,6 @@ int simplified_flarepp_mixer_fwd_train(int64_t B, int64_t H, int64_t N, int64_t 
     if (!saved) return FLAREPP_ERR_INVALID_ARGUMENT;
     return mixer_impl(B, H, N, M, D, dtype, q0, nullptr, nullptr, k0, v0, k, v, y, workspace,
                       workspace_bytes, stream, nullptr, saved, saved_bytes);
-  } catch (...) {
-    return FLAREPP_ERR_HIP;
-  }
-}
-
-int simplified_flarepp_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
-                                 int dtype, const void* q0, const void* k0, const void* v0,
-                                 const void* k, const void* v, const void* y, const void* dy,
-                                 const float* saved, size_t saved_bytes, float* dq0, float* dk0,
-                                 float* dv0, float* dk, float* dv, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  try {
-    if (!q0 || !k0 || !v0) return FLAREPP_ERR_INVALID_ARGUMENT;
-    if (k0 == v0) return FLAREPP_ERR_INVALID_ARGUMENT;  // the FLARE++ entry point covers v0 == k0
-    return bwd_impl(B, H, N, M, D, dtype, (float)(1.0 / std::sqrt((double)D)), q0, nullptr, k0,
-                    v0, nullptr, k, v, y, dy, saved, saved_bytes, dq0, nullptr, nullptr, dk0,
-                    dv0, dk, dv, workspace, workspace_bytes, stream);
   } catch (...) {
     return FLAREPP_ERR_HIP;
   }
