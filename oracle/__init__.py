@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the FLARE++ mixer forward pass and its gradients.
+"""fp64 CPU oracle for the FLARE++ mixer forward pass, its gradients and
+its front end (input projections and head-wise normalisation).
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check in
 __graft_entry__ and by the CPU-baseline leg of bench.py, never by the GPU
@@ -8,5 +9,7 @@ from .flarepp_oracle import *  # noqa: F401,F403
 from .flarepp_backward import *  # noqa: F401,F403
 from .flarepp_oracle import __all__ as _fwd_all
 from .flarepp_backward import __all__ as _bwd_all
+from .flarepp_frontend import *  # noqa: F401,F403
+from .flarepp_frontend import __all__ as _fe_all
 
-__all__ = list(_fwd_all) + list(_bwd_all)
+__all__ = list(_fwd_all) + list(_bwd_all) + list(_fe_all)
