@@ -13,6 +13,9 @@ Prints one JSON line on stdout; progress goes to stderr.
   python bench.py --backward [--steps K] [--warmup W] [--workload NAME]
                   (times flarepp_mixer_bwd alone: one training forward fills
                    the saved tensors, then K backward calls are timed)
+  python bench.py --frontend [--steps K] [--warmup W] [--workload NAME]
+                  (times flarepp_frontend_fwd, the three projections of the
+                   block input x [B, N, H*D] with k0 normalised head-wise)
 """
 
 from __future__ import annotations
@@ -69,12 +72,13 @@ class HipEvents:
 
 
 def source_digest() -> str:
-    """Digest of the forward's sources (kernels, shared headers, the forward
-    launch plan); the backward's own files are left out."""
+    """Digest of the mixer forward's sources (kernels, shared headers, the
+    forward launch plan); the backward's and the front end's own files are
+    left out."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_latent_attention_mixer_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.startswith("backward"):
+        if f.startswith(("backward", "frontend")):
             continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
@@ -220,6 +224,54 @@ def bench_backward(a, fp, torch, np, w, x, args, y, ws):
     return 0
 
 
+def bench_frontend(a, fp, torch, w):
+    """Times K flarepp_frontend_fwd calls at the workload's block width
+    (C = H D); prints one JSON line with the HBM roofline."""
+    from flarepp_workloads import make_frontend_inputs
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
+    C = w.H * w.D
+    log(f"[bench] front end: B={w.B} N={w.N} C={C} H={w.H} D={w.D} {w.dtype}")
+    x = make_frontend_inputs(w.B, w.N, C, w.H, w.D, w.dtype, seed=w.seed + 200)
+    d = {n: torch.from_numpy(x[n]).to(dev).to(tdt) for n in
+         ("x", "w_k0", "w_k", "w_v", "b_k0", "b_k", "b_v", "g_k0")}
+    out = tuple(torch.empty((w.B, w.H, w.N, w.D), dtype=tdt, device=dev) for _ in range(3))
+    call = lambda: fp.flarepp_frontend_fwd(d["x"], d["w_k0"], d["w_k"], d["w_v"], w.H,
+                                           b_k0=d["b_k0"], b_k=d["b_k"], b_v=d["b_v"],
+                                           g_k0=d["g_k0"], eps=1e-6, out=out)
+    for _ in range(a.warmup):
+        call()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(a.steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / a.steps
+    T = w.B * w.N
+    e = 2
+    nbytes = T * C * e + 3 * w.H * w.D * C * e + 3 * T * w.H * w.D * e
+    flops = 2 * T * C * 3 * w.H * w.D
+    t = ms / 1e3
+    result = {
+        "metric": "FLARE++ block front end (3 projections + head-wise norm) tokens/s, 1 GPU",
+        "value": round(T / t, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "C": C, "H": w.H, "D": w.D,
+                   "dtype": w.dtype, "pass": "frontend"},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "tflops": round(flops / t / 1e12, 2),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +282,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
     ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--frontend", action="store_true")
     a = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -252,6 +305,8 @@ def main(argv=None):
         return 1
     fp.load_library()
     w = WORKLOADS[a.workload]
+    if a.frontend:
+        return bench_frontend(a, fp, torch, w)
     dev = torch.device("cuda:0")
     tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
     log(f"[bench] generating {w.name} {w.shape_dict} {w.dtype}")

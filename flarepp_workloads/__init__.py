@@ -201,3 +201,22 @@ def make_cotangent(B, H, N, D, dtype, seed, scale=1.0):
     ``dtype`` (float32 array holding dtype-exact values)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return round_to_dtype(_normal(rng, (B, H, N, D), scale), dtype)
+
+
+def make_frontend_inputs(B, N, C, H, D, dtype, seed, bias=True, gain=True):
+    """Seeded inputs of the block front end: x [B,N,C] ~ N(0,1), the three
+    linear-layer weights [H*D, C] ~ N(0, 1/C), biases [H*D] ~ N(0, 0.1^2)
+    (or None), the k0 normalisation gain [H, D] ~ U[0.5, 1.5) (or None);
+    drawn in that order and rounded to ``dtype``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = dict(x=_normal(rng, (B, N, C)))
+    for name in ("w_k0", "w_k", "w_v"):
+        out[name] = _normal(rng, (H * D, C), 1.0 / math.sqrt(C))
+    for name in ("b_k0", "b_k", "b_v"):
+        out[name] = _normal(rng, (H * D,), 0.1) if bias else None
+    out["g_k0"] = (rng.random(size=(H, D), dtype=np.float32) + np.float32(0.5)) if gain else None
+    for name, a in list(out.items()):
+        if a is not None:
+            out[name] = round_to_dtype(a, dtype)
+    out.update(dtype=dtype, B=B, N=N, C=C, H=H, D=D)
+    return out

@@ -311,6 +311,39 @@ int simplified_flarepp_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int
                                  float* dv0, float* dk, float* dv, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Front end of the block (FLARE.py README, "FLARE++": three input
+ * projections, the synthesis keys and values shared; the synthesis call
+ * normalised head by head -- its exact form is in the paper's Appendix A,
+ * which the pages do not include).  Reading taken: a projection is
+ * x @ W^T + b with W in the [H*D, C] layout of a linear layer, split into H
+ * heads of D features (head-major); the head-wise normalisation is
+ * u / sqrt(mean_d(u_d^2) + eps) * g over the D features of one head, applied
+ * to k0 and to the seeds q0, not to k or v.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * k0, k, v = the three projections of the block input x, k0 normalised.
+ *   x                 : [B, N, C] dtype (C a multiple of 16)
+ *   w_k0, w_k, w_v    : [H*D, C] dtype;  b_k0, b_k, b_v : [H*D] dtype or NULL
+ *   g_k0              : [H, D] dtype gain, or NULL (gain 1)
+ *   eps               : > 0 (checked when normalize_k0 != 0)
+ *   k0, k, v          : [B, H, N, D] dtype, written; must not overlap any
+ *                       input or each other
+ * bf16/fp16, D in {16, 32, 64}; all tensors 16-byte aligned.  fp32 and other
+ * D return FLAREPP_ERR_UNSUPPORTED.  One launch on `stream`, no workspace.
+ */
+int flarepp_frontend_fwd(int64_t B, int64_t N, int64_t C, int64_t H, int64_t D, int dtype,
+                         const void* x, const void* w_k0, const void* w_k, const void* w_v,
+                         const void* b_k0, const void* b_k, const void* b_v, const void* g_k0,
+                         float eps, int normalize_k0, void* k0, void* k, void* v, void* stream);
+
+/* Head-wise normalisation of the seeds: q0_out = q0 / sqrt(mean_d(q0^2) +
+ * eps) * g per (h, m); q0 [H, M, D] dtype, g [H, D] or NULL, D <= 64;
+ * q0_out may be q0 itself (in place) but must not overlap it otherwise. */
+int flarepp_seed_norm_fwd(int64_t H, int64_t M, int64_t D, int dtype, const void* q0,
+                          const void* g_q0, float eps, void* q0_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,6 +31,7 @@ __all__ = [
     "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
     "flarepp_mixer_fwd_train", "flarepp_mixer_bwd", "flare_mixer_fwd_train", "flare_mixer_bwd",
     "simplified_flarepp_mixer_fwd_train", "simplified_flarepp_mixer_bwd",
+    "flarepp_frontend_fwd", "flarepp_seed_norm_fwd",
     "flarepp_workspace_size", "flare_encode_workspace_size", "flare_decode_workspace_size",
     "flarepp_status_string", "flarepp_version", "declared_functions",
     "FLAREPP_OK", "FLAREPP_ERR_INVALID_ARGUMENT", "FLAREPP_ERR_UNSUPPORTED",
@@ -106,6 +107,10 @@ def load_library():
     lib.simplified_flarepp_mixer_fwd_train.restype = i32
     lib.simplified_flarepp_mixer_bwd.argtypes = shape + [i32] + [vp] * 7 + [vp, sz] + [vp] * 5 + [vp, sz, vp]
     lib.simplified_flarepp_mixer_bwd.restype = i32
+    lib.flarepp_frontend_fwd.argtypes = [i64] * 5 + [i32] + [vp] * 8 + [f32, i32] + [vp] * 4
+    lib.flarepp_frontend_fwd.restype = i32
+    lib.flarepp_seed_norm_fwd.argtypes = [i64] * 3 + [i32, vp, vp, f32, vp, vp]
+    lib.flarepp_seed_norm_fwd.restype = i32
     lib.flare_mixer_fwd.argtypes = shape + [i32, f32] + [vp] * 4 + [vp, sz, vp]
     lib.flare_mixer_fwd.restype = i32
     lib.flare_encode_fwd.argtypes = shape + [i32, f32, vp, i64, vp, vp, vp, i64, vp, sz, vp]
@@ -512,3 +517,55 @@ def simplified_flarepp_mixer_bwd(q0, k0, v0, k, v, y, dy, saved, workspace=None,
           saved.numel() * 4, _ptr(g["dq0"]), _ptr(g["dk0"]), _ptr(g["dv0"]), _ptr(g["dk"]),
           _ptr(g["dv"]), _ptr(ws), ws.numel(), _stream(stream))
     return g
+
+
+# --------------------------------------------------------------------------
+# front end: projections and head-wise normalisation
+# --------------------------------------------------------------------------
+
+def flarepp_frontend_fwd(x, w_k0, w_k, w_v, H, b_k0=None, b_k=None, b_v=None, g_k0=None,
+                         eps=1e-6, normalize_k0=True, out=None, stream=None):
+    """k0, k, v [B,H,N,D] from x [B,N,C] and linear-layer weights [H*D, C];
+    k0 normalised head-wise (see include/flarepp.h)."""
+    import torch
+    lib = load_library()
+    B, N, C = x.shape
+    HD = w_k0.shape[0]
+    if HD % H:
+        raise ValueError(f"weight rows {HD} are not a multiple of H={H}")
+    D = HD // H
+    dev, dt = x.device, x.dtype
+    _check_tensor("x", x, (B, N, C), dt, dev)
+    for name, t in (("w_k0", w_k0), ("w_k", w_k), ("w_v", w_v)):
+        _check_tensor(name, t, (HD, C), dt, dev)
+    for name, t in (("b_k0", b_k0), ("b_k", b_k), ("b_v", b_v)):
+        if t is not None:
+            _check_tensor(name, t, (HD,), dt, dev)
+    if g_k0 is not None:
+        _check_tensor("g_k0", g_k0, (H, D), dt, dev)
+    if out is None:
+        out = tuple(torch.empty((B, H, N, D), dtype=dt, device=dev) for _ in range(3))
+    for name, t in zip(("k0", "k", "v"), out):
+        _check_tensor(name, t, (B, H, N, D), dt, dev)
+    opt = lambda t: None if t is None else _ptr(t)
+    _call(lib.flarepp_frontend_fwd, "flarepp_frontend_fwd", B, N, C, H, D, dtype_code(x),
+          _ptr(x), _ptr(w_k0), _ptr(w_k), _ptr(w_v), opt(b_k0), opt(b_k), opt(b_v), opt(g_k0),
+          float(eps), 1 if normalize_k0 else 0, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+          _stream(stream))
+    return out
+
+
+def flarepp_seed_norm_fwd(q0, g=None, eps=1e-6, out=None, stream=None):
+    """Head-wise normalisation of the seeds q0 [H, M, D]; out may be q0."""
+    import torch
+    lib = load_library()
+    H, M, D = q0.shape
+    _check_tensor("q0", q0, (H, M, D), q0.dtype, q0.device)
+    if g is not None:
+        _check_tensor("g", g, (H, D), q0.dtype, q0.device)
+    if out is None:
+        out = torch.empty_like(q0)
+    _check_tensor("out", out, (H, M, D), q0.dtype, q0.device)
+    _call(lib.flarepp_seed_norm_fwd, "flarepp_seed_norm_fwd", H, M, D, dtype_code(q0), _ptr(q0),
+          None if g is None else _ptr(g), float(eps), _ptr(out), _stream(stream))
+    return out

@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflarepp.so")
 
 SOURCES = ["encode_split.hip", "combine.hip", "decode.hip", "backward.hip", "flarepp_abi.cpp",
-           "backward_abi.cpp"]
+           "backward_abi.cpp", "frontend.hip", "frontend_abi.cpp"]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

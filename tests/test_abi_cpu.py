@@ -259,3 +259,42 @@ def test_simplified_bwd_validates():
     import torch
     if not torch.cuda.is_available():
         assert call() == HIP
+
+
+# ---------------------------------------------------------------- front end
+FE = {name: ctypes.c_void_p(0x10000000 * (i + 40)) for i, name in
+      enumerate(["x", "w0", "w1", "w2", "b0", "b1", "b2", "g", "o0", "o1", "o2"])}
+
+
+def _fe(B=1, N=100, C=64, H=2, D=32, dt=1, eps=1e-6, norm=1, **kw):
+    n = dict(x="x", w0="w0", w1="w1", w2="w2", b0="b0", b1="b1", b2="b2", g="g", o0="o0",
+             o1="o1", o2="o2")
+    n.update(kw)
+    P = lambda k: None if n[k] is None else (n[k] if isinstance(n[k], ctypes.c_void_p) else FE[n[k]])
+    return lib().flarepp_frontend_fwd(B, N, C, H, D, dt, P("x"), P("w0"), P("w1"), P("w2"),
+                                      P("b0"), P("b1"), P("b2"), P("g"), eps, norm, P("o0"),
+                                      P("o1"), P("o2"), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), INV), (dict(w1=None), INV), (dict(o2=None), INV), (dict(dt=0), UNS),
+    (dict(dt=5), INV), (dict(D=8), UNS), (dict(C=24), UNS), (dict(N=0), INV),
+    (dict(eps=0.0), INV), (dict(eps=float("nan")), INV), (dict(o1="o0"), INV),
+    (dict(o0="x"), INV), (dict(o2="w1"), INV),
+    (dict(x=ctypes.c_void_p(0x10000000 * 40 + 8)), INV),     # misaligned x
+])
+def test_frontend_rejects_before_any_launch(kw, code):
+    assert _fe(**kw) == code
+
+
+def test_frontend_optional_arguments_and_device():
+    import torch
+    # biases, gain and eps are optional without normalisation
+    st = _fe(b0=None, b1=None, b2=None, g=None, eps=0.0, norm=0)
+    assert st == (HIP if not torch.cuda.is_available() else st)
+    L = lib()
+    assert L.flarepp_seed_norm_fwd(2, 10, 65, 1, FE["x"], None, 1e-6, FE["o0"], None) == UNS
+    assert L.flarepp_seed_norm_fwd(2, 10, 32, 1, FE["x"], None, 0.0, FE["o0"], None) == INV
+    assert L.flarepp_seed_norm_fwd(2, 10, 32, 0, FE["x"], None, 1e-6, FE["o0"], None) == UNS
+    if not torch.cuda.is_available():
+        assert L.flarepp_seed_norm_fwd(2, 10, 32, 1, FE["x"], None, 1e-6, FE["x"], None) == HIP
