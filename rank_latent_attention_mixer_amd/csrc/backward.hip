@@ -195,8 +195,15 @@ __device__ __forceinline__ void store_acc_row(float* dst, const f32x16 (&acc)[ND
 constexpr int kBwdWaves = 8;
 constexpr int kBwdTile = 128;  // tokens per LDS tile
 
+// Waves (32 latents each) per latent-pass workgroup: 16 where the kernel
+// fits 128 VGPRs (four waves per SIMD, each token tile shared by twice the
+// latents), 8 at D = 64.
+template <int D>
+constexpr int lat_waves() { return D <= 32 ? 16 : 8; }
+
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_lat_kernel(BwdLatParams a) {
+__global__ __launch_bounds__(64 * lat_waves<D>()) void bwd_lat_kernel(BwdLatParams a) {
+  constexpr int NWV = lat_waves<D>();
   using O = LdsOps<T, D>;
   using V8 = typename O::V8;
   using L = RowLayout<D>;
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lat_kernel(BwdLatParams a)
   const int b = set / a.H, hd = set - b * a.H;
   // closed gate (synthesis pass): the partials of this head are zero
   const bool closed = a.gate != nullptr && gate_sigma(a.gate[hd]) == 0.f;
-  const int col = blockIdx.y * 32 * kBwdWaves + wave * 32 + r;      // latent of this lane
+  const int col = blockIdx.y * 32 * NWV + wave * 32 + r;            // latent of this lane
   const int colc = min(col, a.M - 1);
 
   V8 qop[KD], gop[KD];
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lat_kernel(BwdLatParams a)
   // tile staging through registers: 16-byte chunks, thread-strided; the
   // rows past the chunk's end repeat its last token (their weights are 0)
   constexpr int CH = kBwdTile * L::CPR;                      // chunks per tensor per tile
-  constexpr int PER = (CH + 64 * kBwdWaves - 1) / (64 * kBwdWaves);
+  constexpr int PER = (CH + 64 * NWV - 1) / (64 * NWV);
   u32x4 stage[NT][PER];
   float sv0 = 0.f, sv1 = 0.f;
   auto fetch = [&](int tile) {
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lat_kernel(BwdLatParams a)
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int e = tid + i * 64 * kBwdWaves;
+        const int e = tid + i * 64 * NWV;
         if (e < CH) {
           const int row = e / L::CPR, c = e - row * L::CPR;
           stage[t][i] = ldg16(tbase[t] + ((int64_t)(tile * kBwdTile + min(row, lim)) * D + 8 * c) * 2);
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lat_kernel(BwdLatParams a)
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int e = tid + i * 64 * kBwdWaves;
+        const int e = tid + i * 64 * NWV;
         if (e < CH) {
           const int row = e / L::CPR, c = e - row * L::CPR;
           *reinterpret_cast<u32x4*>(&lds[buf][t * TB + L::offset(row, 16 * c)]) = stage[t][i];
@@ -341,8 +348,15 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lat_kernel(BwdLatParams a)
 // ---------------------------------------------------------------------------
 // Tokens in registers, all latents resident in LDS.
 // ---------------------------------------------------------------------------
+// Waves per token-pass workgroup: the workgroup holds every latent of its
+// head in LDS, so it is the only one on its CU; the synthesis pass is small
+// enough in registers (<= 128 VGPRs) to run four waves per SIMD.
+template <int MODE, int D>
+constexpr int tok_waves() { return (MODE == kBwdTokSyn && D <= 32) ? 16 : 8; }
+
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_tok_kernel(BwdTokParams a) {
+__global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(BwdTokParams a) {
+  constexpr int NWV = tok_waves<MODE, D>();
   using O = LdsOps<T, D>;
   using V8 = typename O::V8;
   using L = RowLayout<D>;
@@ -357,7 +371,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_tok_kernel(BwdTokParams a)
   const int set = blockIdx.x / a.wg_per_bh;
   const int part = blockIdx.x - set * a.wg_per_bh;
   const int b = set / a.H, hd = set - b * a.H;
-  constexpr int kTok = 32 * kBwdWaves;
+  constexpr int kTok = 32 * NWV;
   const int64_t ntiles = (a.N + kTok - 1) / kTok;
   const bool closed = a.gate != nullptr && gate_sigma(a.gate[hd]) == 0.f;
 
@@ -371,14 +385,14 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_tok_kernel(BwdTokParams a)
       if (a.lat[t] == nullptr) continue;
       const unsigned char* src = reinterpret_cast<const unsigned char*>(a.lat[t]) +
                                  2 * (b * a.lat_b_stride[t] + hd * a.lat_h_stride[t]);
-      for (int e = tid; e < CH; e += 64 * kBwdWaves) {
+      for (int e = tid; e < CH; e += 64 * NWV) {
         const int row = e / L::CPR, c = e - row * L::CPR;
         const u32x4 v = row < a.M ? ldg16(src + ((int64_t)row * D + 8 * c) * 2)
                                   : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(&lds_raw[t * TB + L::offset(row, 16 * c)]) = v;
       }
     }
-    for (int m = tid; m < Mk; m += 64 * kBwdWaves) {
+    for (int m = tid; m < Mk; m += 64 * NWV) {
       const bool in = m < a.M;
       vec[m] = in ? a.shift - a.lat_lse[(int64_t)set * a.M + m] : 0.f;
       vec[Mk + m] = in ? a.lat_negd[(int64_t)set * a.M + m] : 0.f;
@@ -648,9 +662,9 @@ __global__ __launch_bounds__(256) void bwd_norm_kernel(BwdNormParams a) {
 template <int MODE, typename T>
 hipError_t lat_d(int D, const BwdLatParams& p, dim3 grid, hipStream_t s) {
   switch (D) {
-    case 16: hipLaunchKernelGGL((bwd_lat_kernel<T, 16, MODE>), grid, dim3(64 * kBwdWaves), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((bwd_lat_kernel<T, 32, MODE>), grid, dim3(64 * kBwdWaves), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((bwd_lat_kernel<T, 64, MODE>), grid, dim3(64 * kBwdWaves), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((bwd_lat_kernel<T, 16, MODE>), grid, dim3(64 * lat_waves<16>()), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((bwd_lat_kernel<T, 32, MODE>), grid, dim3(64 * lat_waves<32>()), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((bwd_lat_kernel<T, 64, MODE>), grid, dim3(64 * lat_waves<64>()), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -670,7 +684,7 @@ hipError_t tok_launch(const BwdTokParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(p.B * p.H * p.wg_per_bh));
-  hipLaunchKernelGGL((bwd_tok_kernel<T, D, MODE>), grid, dim3(64 * kBwdWaves), lds, s, p);
+  hipLaunchKernelGGL((bwd_tok_kernel<T, D, MODE>), grid, dim3(64 * tok_waves<MODE, D>()), lds, s, p);
   return hipGetLastError();
 }
 
@@ -686,13 +700,13 @@ hipError_t tok_d(int D, const BwdTokParams& p, hipStream_t s) {
 
 }  // namespace
 
-int bwd_latents_per_block() { return 32 * kBwdWaves; }
+int bwd_latents_per_block(int D) { return 32 * (D <= 32 ? lat_waves<32>() : lat_waves<64>()); }
 int bwd_tokens_per_tile() { return 32 * kBwdWaves; }
 size_t bwd_tok_lds_bytes(int M, int D) { return tok_lds(M, D); }
 
 hipError_t launch_bwd_lat(int dtype, int mode, int D, const BwdLatParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.H * p.nchunks),
-                  (unsigned)((p.M + 32 * kBwdWaves - 1) / (32 * kBwdWaves)));
+  const int lpb = bwd_latents_per_block(D);
+  const dim3 grid((unsigned)(p.B * p.H * p.nchunks), (unsigned)((p.M + lpb - 1) / lpb));
   if (dtype == kBF16) {
     if (mode == kBwdLatDec) return lat_d<kBwdLatDec, __bf16>(D, p, grid, s);
     if (mode == kBwdLatEnc) return lat_d<kBwdLatEnc, __bf16>(D, p, grid, s);

@@ -141,7 +141,7 @@ hipError_t launch_bwd_dec_sums(const BwdSumsParams& p, hipStream_t s);
 hipError_t launch_bwd_add_sums(const BwdAddParams& p, hipStream_t s);
 hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s);
 hipError_t launch_bwd_norm(const BwdNormParams& p, hipStream_t s);
-int bwd_latents_per_block();
+int bwd_latents_per_block(int D);
 int bwd_tokens_per_tile();
 size_t bwd_tok_lds_bytes(int M, int D);
 

@@ -34,7 +34,7 @@ int make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dty
   p->B = B; p->H = H; p->N = N; p->M = M; p->D = D; p->dtype = dtype;
   p->Mpad = (int)((M + 31) / 32 * 32);
   const int64_t BH = B * H;
-  p->mblocks = (int)((M + bwd_latents_per_block() - 1) / bwd_latents_per_block());
+  p->mblocks = (int)((M + bwd_latents_per_block((int)D) - 1) / bwd_latents_per_block((int)D));
   const int64_t unit = 128;
   const int64_t tiles = (N + unit - 1) / unit;
   int64_t c = (kBwdTargetWgs + BH * p->mblocks - 1) / (BH * p->mblocks);
