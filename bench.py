@@ -16,6 +16,8 @@ Prints one JSON line on stdout; progress goes to stderr.
   python bench.py --frontend [--steps K] [--warmup W] [--workload NAME]
                   (times flarepp_frontend_fwd, the three projections of the
                    block input x [B, N, H*D] with k0 normalised head-wise)
+  python bench.py --probe   (measured dense bf16 MFMA and v_exp_f32 rates of
+                             this device, beside the published peak)
 """
 
 from __future__ import annotations
@@ -78,7 +80,7 @@ def source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_latent_attention_mixer_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.startswith(("backward", "frontend")):
+        if f.startswith(("backward", "frontend")) or not os.path.isfile(os.path.join(csrc, f)):
             continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
@@ -224,6 +226,47 @@ def bench_backward(a, fp, torch, np, w, x, args, y, ws):
     return 0
 
 
+def probe_peaks():
+    """Measured matrix-core and exponential rates (libflarepp_probe.so):
+    1024 workgroups of 4 waves (four per SIMD), long independent chains."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "rank_latent_attention_mixer_amd", "libflarepp_probe.so"))
+    lib.flarepp_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.flarepp_probe_work.restype = ctypes.c_double
+    lib.flarepp_probe_work.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    blocks, iters = 1024, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for which, name in ((0, "mfma_bf16"), (1, "exp_f32")):
+        for _ in range(2):
+            if lib.flarepp_probe_launch(which, blocks, iters, ctypes.c_void_p(out.data_ptr()), stream):
+                raise RuntimeError("probe launch failed")
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(10):
+            lib.flarepp_probe_launch(which, blocks, iters, ctypes.c_void_p(out.data_ptr()), stream)
+        stop.record()
+        torch.cuda.synchronize()
+        t = start.elapsed_time(stop) / 10 / 1e3
+        res[name] = lib.flarepp_probe_work(which, blocks, iters) / t
+        log(f"[probe] {name}: {t * 1e3:.3f} ms per launch")
+    from flarepp_workloads import WORKLOADS
+    w = WORKLOADS["million_token_bf16"]
+    exps = 3 * w.B * w.H * w.N * w.M  # one forward, every gate open
+    print(json.dumps({
+        "probe": "dense bf16 v_mfma_f32_32x32x16 and v_exp_f32 throughput, 1 GPU",
+        "mfma_bf16_tflops_measured": round(res["mfma_bf16"] / 1e12, 1),
+        "mfma_bf16_tflops_published": PEAK_BF16_TFLOPS,
+        "exp_f32_per_s_measured": float(f"{res['exp_f32']:.4g}"),
+        "exp_ms_per_million_token_forward": float(f"{exps / res['exp_f32'] * 1e3:.4g}"),
+    }), flush=True)
+    return 0
+
+
 def bench_frontend(a, fp, torch, w):
     """Times K flarepp_frontend_fwd calls at the workload's block width
     (C = H D); prints one JSON line with the HBM roofline."""
@@ -283,6 +326,7 @@ def main(argv=None):
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
     ap.add_argument("--backward", action="store_true")
     ap.add_argument("--frontend", action="store_true")
+    ap.add_argument("--probe", action="store_true")
     a = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -293,6 +337,8 @@ def main(argv=None):
 
     if a.copy_calibration_mib > 0:
         return copy_calibration(a.copy_calibration_mib)
+    if a.probe:
+        return probe_peaks()
 
     import numpy as np
     import torch
