@@ -298,3 +298,27 @@ def test_frontend_optional_arguments_and_device():
     assert L.flarepp_seed_norm_fwd(2, 10, 32, 0, FE["x"], None, 1e-6, FE["o0"], None) == UNS
     if not torch.cuda.is_available():
         assert L.flarepp_seed_norm_fwd(2, 10, 32, 1, FE["x"], None, 1e-6, FE["x"], None) == HIP
+
+
+def test_probe_library_exports_its_header():
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    text = open(os.path.join(root, "include", "flarepp_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(flarepp_probe\w*)\s*\(", text)))
+    assert names == ["flarepp_probe_launch", "flarepp_probe_work"]
+    path = os.path.join(os.path.dirname(fp.library_path()), "libflarepp_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libflarepp_probe.so not built")
+    P = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(P, n), n
+    P.flarepp_probe_work.restype = ctypes.c_double
+    P.flarepp_probe_work.argtypes = [ctypes.c_int] * 3
+    # 1 workgroup of 4 waves, 1 iteration: 4 x 8 products of 2*32*32*16 flops
+    assert P.flarepp_probe_work(0, 1, 1) == 4 * 8 * 2 * 32 * 32 * 16
+    assert P.flarepp_probe_work(1, 2, 3) == 2 * 256 * 3 * 8
+    P.flarepp_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    assert P.flarepp_probe_launch(0, 0, 1, None, None) == 1   # rejected before any launch
+    assert P.flarepp_probe_launch(7, 1, 1, ctypes.c_void_p(0x1000), None) == 1
