@@ -6,6 +6,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <initializer_list>
 
 #include "../../include/flarepp.h"
 
@@ -74,6 +75,26 @@ inline Saved saved_layout(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
     const hipError_t e_ = (expr);                \
     if (e_ != hipSuccess) return FLAREPP_ERR_HIP; \
   } while (0)
+
+// A caller buffer: address and bytes (null or empty: not present).
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// True if an output buffer overlaps another output or any input (inputs
+// include the workspace and saved tensors).  Outputs are written by the
+// kernels, so any such overlap would corrupt a result.
+inline bool outputs_alias(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    if (!o->p || !o->n) continue;
+    for (auto q = o + 1; q != outs.end(); ++q)
+      if (q->p && q->n && overlaps(o->p, o->n, q->p, q->n)) return true;
+    for (const Span& i : ins)
+      if (i.p && i.n && overlaps(o->p, o->n, i.p, i.n)) return true;
+  }
+  return false;
+}
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 

@@ -103,17 +103,15 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   for (const void* in : {k, v, y, dy, pp ? k0 : nullptr, pp ? v0 : nullptr})
     if (in && !aligned16(in)) return FLAREPP_ERR_INVALID_ARGUMENT;
   const size_t tokf = (size_t)(B * H * N * D) * 4, latf = (size_t)(H * M * D) * 4;
-  const size_t toke = (size_t)(B * H * N * D) * 2;
-  for (const void* g : {(const void*)dk, (const void*)dv, pp ? (const void*)dk0 : nullptr,
-                        simplified ? (const void*)dv0 : nullptr}) {
-    if (!g) continue;
-    for (const void* in : {k, v, y, dy, pp ? k0 : nullptr, pp ? v0 : nullptr})
-      if (in && overlaps(g, tokf, in, toke)) return FLAREPP_ERR_INVALID_ARGUMENT;
-    if (overlaps(g, tokf, saved, sv.floats * 4)) return FLAREPP_ERR_INVALID_ARGUMENT;
-  }
-  if (dq_lat && overlaps(dq_lat, latf, saved, sv.floats * 4)) return FLAREPP_ERR_INVALID_ARGUMENT;
+  const size_t toke = (size_t)(B * H * N * D) * 2, late = (size_t)(H * M * D) * 2;
   if (ws == nullptr || ws_bytes < p.total || ((uintptr_t)ws % kAlign) != 0)
     return FLAREPP_ERR_WORKSPACE;
+  if (outputs_alias({{dq0, pp ? latf : 0}, {dq_lat, latf}, {dgate, dgate ? (size_t)H * 4 : 0},
+                     {dk0, pp ? tokf : 0}, {dv0, simplified ? tokf : 0}, {dk, tokf}, {dv, tokf}},
+                    {{q0, late}, {gate, gate ? (size_t)H * 4 : 0}, {k0, toke}, {v0, toke},
+                     {q_flare, late}, {k, toke}, {v, toke}, {y, toke}, {dy, toke},
+                     {saved, sv.floats * 4}, {ws, ws_bytes}}))
+    return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_device()) != FLAREPP_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -194,12 +194,13 @@ int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
     return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_workspace(p, ws, ws_bytes)) != FLAREPP_OK) return st;
   Saved sv = saved_layout(B, H, N, M, D, saved);
-  if (saved) {
-    if (saved_bytes < sv.floats * sizeof(float) || (reinterpret_cast<uintptr_t>(saved) & 15))
-      return FLAREPP_ERR_WORKSPACE;
-    if (overlaps(saved, sv.floats * 4, y, tok) || overlaps(saved, sv.floats * 4, ws, ws_bytes))
-      return FLAREPP_ERR_INVALID_ARGUMENT;
-  }
+  if (saved && (saved_bytes < sv.floats * sizeof(float) ||
+                (reinterpret_cast<uintptr_t>(saved) & 15)))
+    return FLAREPP_ERR_WORKSPACE;
+  if (outputs_alias({{y, tok}, {saved, saved ? sv.floats * 4 : 0}},
+                    {{q0, lat}, {q_fixed, lat}, {gate, gate ? (size_t)H * 4 : 0}, {k0, tok},
+                     {v0, tok}, {k, tok}, {v, tok}, {ws, ws_bytes}}))
+    return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_device()) != FLAREPP_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -264,12 +265,12 @@ int flare_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
     return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_workspace(p, ws, ws_bytes)) != FLAREPP_OK) return st;
   Saved sv = saved_layout(B, H, N, M, D, saved);
-  if (saved) {
-    if (saved_bytes < sv.floats * sizeof(float) || (reinterpret_cast<uintptr_t>(saved) & 15))
-      return FLAREPP_ERR_WORKSPACE;
-    if (overlaps(saved, sv.floats * 4, y, tok) || overlaps(saved, sv.floats * 4, ws, ws_bytes))
-      return FLAREPP_ERR_INVALID_ARGUMENT;
-  }
+  if (saved && (saved_bytes < sv.floats * sizeof(float) ||
+                (reinterpret_cast<uintptr_t>(saved) & 15)))
+    return FLAREPP_ERR_WORKSPACE;
+  if (outputs_alias({{y, tok}, {saved, saved ? sv.floats * 4 : 0}},
+                    {{q, lat}, {k, tok}, {v, tok}, {ws, ws_bytes}}))
+    return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_device()) != FLAREPP_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -390,6 +391,7 @@ int flare_encode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
     if (overlaps(z, zb, k, tok) || overlaps(z, zb, v, tok) || overlaps(z, zb, q, lat))
       return FLAREPP_ERR_INVALID_ARGUMENT;
     if ((st = check_workspace(p, workspace, workspace_bytes)) != FLAREPP_OK) return st;
+    if (overlaps(z, zb, workspace, workspace_bytes)) return FLAREPP_ERR_INVALID_ARGUMENT;
     if ((st = check_device()) != FLAREPP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float c = (float)((double)scale * 1.4426950408889634);
@@ -426,6 +428,7 @@ int flare_decode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
     if (overlaps(y, tok, k, tok) || overlaps(y, tok, z, zb) || overlaps(y, tok, q, lat))
       return FLAREPP_ERR_INVALID_ARGUMENT;
     if ((st = check_workspace(p, workspace, workspace_bytes)) != FLAREPP_OK) return st;
+    if (overlaps(y, tok, workspace, workspace_bytes)) return FLAREPP_ERR_INVALID_ARGUMENT;
     if ((st = check_device()) != FLAREPP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float c = (float)((double)scale * 1.4426950408889634);

@@ -94,6 +94,7 @@ def _mixer(B=1, H=2, N=1024, M=16, D=8, dt=1, q0="q0", qf="qf", gate="gate", k0=
     (dict(ws=ctypes.c_void_p(0x10000000 * 8 + 64)), WS),     # misaligned workspace
     (dict(y="k"), INV), (dict(y="v"), INV), (dict(y="k0"), INV), (dict(y="q0"), INV),
     (dict(y=ctypes.c_void_p(0x10000000 * 5 + 8)), INV),         # y overlaps k
+    (dict(y="ws"), INV),                                         # y overlaps the workspace
 ])
 def test_mixer_rejects_before_any_launch(kw, code):
     assert _mixer(**kw) == code
@@ -217,6 +218,9 @@ def _bwd(B=1, H=2, N=1024, M=16, D=32, dt=1, saved_bytes=None, wsb=None, **kw):
     (dict(dk="k"), INV), (dict(dv="dy"), INV), (dict(dk0="saved"), INV),
     (dict(dy=ctypes.c_void_p(0x10000000 * 27 + 8)), INV),       # misaligned dy
     (dict(dk=ctypes.c_void_p(0x10000000 * 24 + 4)), INV),       # misaligned dk
+    (dict(dk="bws"), INV),                                        # gradient over the workspace
+    (dict(dq0="dk"), INV), (dict(dgate="dq0"), INV), (dict(dv="dk0"), INV),  # gradients alias
+    (dict(dqf="q0"), INV),                                        # latent gradient over an input
 ])
 def test_bwd_rejects_before_any_launch(kw, code):
     assert _bwd(**kw) == code
