@@ -24,7 +24,7 @@ namespace {
 constexpr int kNC = FLAREPP_DEC_NC;
 // waves per workgroup (build-time knob for D <= 32)
 #ifndef FLAREPP_DEC_WAVES
-#define FLAREPP_DEC_WAVES 12
+#define FLAREPP_DEC_WAVES 16
 #endif
 template <int D>
 struct DecodeWaves {
@@ -39,7 +39,12 @@ struct DecodeLds {
   static int elems(int Mk) { return Mk * KP + DV * zpitch(Mk); }
 };
 
-template <typename T, int D>
+// FIXUP = false: the decoder proper; a wave whose sums leave the fixed
+// reference's range records that tile instead of storing it.
+// FIXUP = true: the same workgroups again, recomputing only the recorded
+// tiles by the exact two-pass method (a workgroup with none exits at once).
+// The split keeps the rare exact path's registers out of the main kernel.
+template <typename T, int D, bool FIXUP>
 __global__ __launch_bounds__(64 * DecodeWaves<D>::value) void
 decode_kernel(DecodeParams a) {
   constexpr int kNW = DecodeWaves<D>::value;
@@ -62,7 +67,23 @@ decode_kernel(DecodeParams a) {
   const int part = blockIdx.x - bh * a.wg_per_bh;
   const int b = bh / a.H, hd = bh - b * a.H;
 
-  // resident latents: q rows [0, Mk) and the value operand rows [0, DV)
+  // this wave's record: bit i = the workgroup's i-th tile (i < 64), and
+  // 1 + the first ordinal >= 64 from which every tile is recomputed (0: none)
+  unsigned long long* rec = a.redo + ((int64_t)blockIdx.x * kNW + wave) * 2;
+  uint64_t fx_bad = 0;
+  int64_t fx_from = -1;
+  if constexpr (FIXUP) {
+    fx_bad = rec[0];
+    fx_from = (int64_t)rec[1] - 1;
+    if (!__syncthreads_or(fx_bad != 0 || fx_from >= 0)) return;  // workgroup-uniform
+  }
+
+  // resident latents: q rows [0, Mk) and the value operand rows [0, DV);
+  // the largest |z| of the head is taken on the way (it bounds every
+  // accumulator, which makes the overflow test per tile a row-sum test)
+  __shared__ unsigned zmax_bits;
+  if (tid == 0) zmax_bits = 0u;
+  __syncthreads();
   {
     const T* qg = reinterpret_cast<const T*>(a.q) + b * a.q_b_stride + hd * a.q_h_stride;
     constexpr int G8 = D / 8;
@@ -72,12 +93,24 @@ decode_kernel(DecodeParams a) {
     }
     const T* zg = reinterpret_cast<const T*>(a.zt) + (int64_t)bh * DV * a.Mpad;
     const int zg8 = Mk / 8;
+    unsigned zb = 0u;  // max over this thread's values of |z| as ordered bits
     for (int u = tid; u < DV * zg8; u += 64 * kNW) {
       const int row = u / zg8, e = u - row * zg8;
-      *reinterpret_cast<u32x4*>(&zs[row * ZP + 8 * e]) = ldg16(zg + (int64_t)row * a.Mpad + 8 * e);
+      const u32x4 v = ldg16(zg + (int64_t)row * a.Mpad + 8 * e);
+      *reinterpret_cast<u32x4*>(&zs[row * ZP + 8 * e]) = v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = (float)__builtin_bit_cast(T, (unsigned short)(v[j] & 0xFFFFu));
+        const float hi = (float)__builtin_bit_cast(T, (unsigned short)(v[j] >> 16));
+        zb = max(zb, max(__float_as_uint(fabsf(lo)), __float_as_uint(fabsf(hi))));
+      }
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) zb = max(zb, (unsigned)__shfl_xor((int)zb, o));
+    if (lane == 0) atomicMax(&zmax_bits, zb);
   }
   __syncthreads();
+  const float zmax = __uint_as_float(zmax_bits);  // NaN bits order above infinity
 
   const T* kg = reinterpret_cast<const T*>(a.k) + (int64_t)bh * a.N * D;
   T* yg = reinterpret_cast<T*>(a.y) + (int64_t)bh * a.N * D;
@@ -136,11 +169,42 @@ decode_kernel(DecodeParams a) {
     }
   };
 
+// y = O / l; lane (h, r) owns columns 32db + 16h .. +15 of token r
+auto store_tile = [&](int64_t nb, const auto& t) {
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb) {
+      const float l = t.row_sum(cb);
+      const float inv = 1.0f / l;
+      const int64_t n = nb + cb * 32 + r;
+      if (a.lse_out && h == 0 && n < a.N)  // saved for the backward pass
+        a.lse_out[(int64_t)bh * a.N + n] = log2f(l) + t.reference(cb);
+      if (n < a.N) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int d0 = 32 * db + 16 * h;
+          if (d0 < D) {
+            T out[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) out[v] = (T)(t.o[db][cb][v] * inv);
+            T* dst = yg + n * D + d0;
+            if constexpr (D >= 16) {
+              *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
+              *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(&out[8]);
+            } else {
+              *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
+            }
+          }
+        }
+      }
+    }
+  };
+
   // One tile: the wave's 32 * kNC token rows arrive as qop (register
-  // operand); sweep all latents and store y.
-  auto process_tile = [&](int64_t tile, const V8 (&qop)[kNC][KD]) {
+  // operand); sweep all latents and store y.  Returns true when the fixed
+  // reference failed (nothing stored; the tile needs the exact path).
+  auto process_tile = [&](int64_t tile, const V8 (&qop)[kNC][KD]) -> bool {
     const int64_t nb = tile * kTokTile + wave * 32 * kNC;
-    if (nb >= a.N) return;  // wave-uniform; no barrier below
+    if (nb >= a.N) return false;  // wave-uniform; no barrier below
     Tile st;
     st.reset();
 #pragma unroll
@@ -207,50 +271,26 @@ decode_kernel(DecodeParams a) {
       vop_at(nfull, vop);
       st.template next<true>(sa, vop, mtail, h);
     }
-    // y = O / l; lane (h, r) owns columns 32db + 16h .. +15 of token r
-    auto store = [&](const auto& t) {
-#pragma unroll
-      for (int cb = 0; cb < kNC; ++cb) {
-        const float l = t.row_sum(cb);
-        const float inv = 1.0f / l;
-        const int64_t n = nb + cb * 32 + r;
-        if (a.lse_out && h == 0 && n < a.N)  // saved for the backward pass
-          a.lse_out[(int64_t)bh * a.N + n] = log2f(l) + t.reference(cb);
-        if (n < a.N) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int d0 = 32 * db + 16 * h;
-            if (d0 < D) {
-              T out[16];
-#pragma unroll
-              for (int v = 0; v < 16; ++v) out[v] = (T)(t.o[db][cb][v] * inv);
-              T* dst = yg + n * D + d0;
-              if constexpr (D >= 16) {
-                *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
-                *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(&out[8]);
-              } else {
-                *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
-              }
-            }
-          }
-        }
-      }
-    };
-    if (!st.overflowed()) {
-      store(st);
-      return;
-    }
-    // sums out of range for the fixed reference: exact two-pass recompute
-    // of this wave's tokens (true maxima over all latents first, then the
-    // sums)
+    if (st.overflowed_bounded(zmax)) return true;  // recomputed exactly in the fix-up pass
+    store_tile(nb, st);
+    return false;
+  };
+
+  // Sums out of range for the fixed reference: exact two-pass recompute of
+  // this wave's tokens of one tile (true maxima over all latents first, then
+  // the sums).  Kept out of the main loop so that its registers are not live
+  // beside the prefetched token rows.
+  auto exact_tile = [&](int64_t tile, const V8 (&qop)[kNC][KD]) {
+    const int64_t nb = tile * kTokTile + wave * 32 * kNC;
     using Exact = FlashTile<T, D, kNC, true>;
     Exact ex;
     ex.reset();
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb)
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd) ex.q[cb][kd] = st.q[cb][kd];
+      for (int kd = 0; kd < KD; ++kd) ex.q[cb][kd] = qop[cb][kd];
     const int ngrp = nfull + (mtail > 0 ? 1 : 0);
+    f32x16 sa[kNC];
     float mx[kNC];
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) mx[cb] = -__builtin_inff();
@@ -273,7 +313,7 @@ decode_kernel(DecodeParams a) {
       vop_at(G, vop);
       ex.template next<true>(sa, vop, a.M - 32 * G, h);
     }
-    store(ex);
+    store_tile(nb, ex);
   };
 
   // The workgroup walks tiles part, part + wg_per_bh, ...; the token rows of
@@ -281,19 +321,44 @@ decode_kernel(DecodeParams a) {
   // current tile is computed (the loop is unrolled by two so the sets never
   // need copying).
   V8 qa[kNC][KD], qb[kNC][KD];
-  int64_t tile = part;
-  load_tokens(tile, qa);
-  while (tile < ntiles) {
-    // issued even past the last tile (rows clamp to N-1, results unused):
-    // no branch, so the waits before each tile count exactly its own loads
-    const int64_t t1 = tile + a.wg_per_bh;
-    load_tokens(t1, qb);
-    process_tile(tile, qa);
-    if (t1 >= ntiles) break;
-    const int64_t t2 = t1 + a.wg_per_bh;
-    load_tokens(t2, qa);
-    process_tile(t1, qb);
-    tile = t2;
+  if constexpr (!FIXUP) {
+    // Tiles that overflowed are remembered by their ordinal i among this
+    // workgroup's tiles (bit i of a mask for i < 64; past that, every tile
+    // from the first such ordinal on).
+    uint64_t bad = 0;
+    int64_t bad_from = -1;
+    auto note_bad = [&](int64_t i) {
+      if (i < 64) bad |= (uint64_t)1 << i;
+      else if (bad_from < 0) bad_from = i;
+    };
+    int64_t tile = part, ord = 0;
+    load_tokens(tile, qa);
+    while (tile < ntiles) {
+      // issued even past the last tile (rows clamp to N-1, results unused):
+      // no branch, so the waits before each tile count exactly its own loads
+      const int64_t t1 = tile + a.wg_per_bh;
+      load_tokens(t1, qb);
+      if (process_tile(tile, qa)) note_bad(ord);
+      if (t1 >= ntiles) break;
+      const int64_t t2 = t1 + a.wg_per_bh;
+      load_tokens(t2, qa);
+      if (process_tile(t1, qb)) note_bad(ord + 1);
+      tile = t2;
+      ord += 2;
+    }
+    if (lane == 0) {  // written for every wave, so no clearing is needed
+      rec[0] = bad;
+      rec[1] = (unsigned long long)(bad_from + 1);
+    }
+  } else {
+    int64_t ord = 0;
+    for (int64_t t = part; t < ntiles; t += a.wg_per_bh, ++ord) {
+      const bool redo =
+          ord < 64 ? ((fx_bad >> ord) & 1) != 0 : (fx_from >= 0 && ord >= fx_from);
+      if (!redo) continue;
+      load_tokens(t, qa);
+      exact_tile(t, qa);
+    }
   }
 }
 
@@ -366,12 +431,15 @@ hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
   const int Mk = (p.M + 31) & ~31;
   const size_t lds = (size_t)DecodeLds<D>::elems(Mk) * sizeof(T);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<T, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    for (const void* f : {(const void*)decode_kernel<T, D, false>,
+                          (const void*)decode_kernel<T, D, true>}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
   }
-  const dim3 grid((unsigned)(p.B * p.H * p.wg_per_bh));
-  hipLaunchKernelGGL((decode_kernel<T, D>), grid, dim3(64 * DecodeWaves<D>::value), lds, s, p);
+  const dim3 grid((unsigned)(p.B * p.H * p.wg_per_bh)), block(64 * DecodeWaves<D>::value);
+  hipLaunchKernelGGL((decode_kernel<T, D, false>), grid, block, lds, s, p);
+  hipLaunchKernelGGL((decode_kernel<T, D, true>), grid, block, lds, s, p);
   return hipGetLastError();
 }
 
@@ -394,6 +462,8 @@ hipError_t launch_f32(const DecodeParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int decode_waves(int D) { return D >= 64 ? DecodeWaves<64>::value : DecodeWaves<32>::value; }
 
 int decode_tokens_per_tile(int D) {
   return 32 * kNC * (D >= 64 ? DecodeWaves<64>::value : DecodeWaves<32>::value);

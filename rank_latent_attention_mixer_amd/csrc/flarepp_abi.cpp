@@ -48,7 +48,7 @@ struct Plan {
   int64_t chunk_tokens;
   int nchunks;
   int dec_wg_per_bh;
-  size_t off_pm, off_pl, off_po, off_q0, off_q, off_z, total;
+  size_t off_pm, off_pl, off_po, off_q0, off_q, off_z, off_redo, total;
 };
 
 int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
@@ -93,6 +93,9 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   p->off_z = off;
   off = align_up(off + (dtype == FLAREPP_F32 ? (size_t)BH * p->Mpad * D * 4
                                              : (size_t)BH * p->DV * p->Mpad * es));
+  // decoder: per (workgroup, wave) record of tiles needing the exact path
+  p->off_redo = off;
+  off = align_up(off + (size_t)BH * w * decode_waves((int)D) * 2 * sizeof(unsigned long long));
   p->total = off;
   return FLAREPP_OK;
 }
@@ -169,6 +172,7 @@ hipError_t decode(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh
   d.lse_out = lse_out;
   d.q = q; d.q_b_stride = qb; d.q_h_stride = qh;
   d.zt = ws_at(ws, p.off_z);
+  d.redo = reinterpret_cast<unsigned long long*>(ws_at(ws, p.off_redo));
   d.k = k; d.y = y;
   d.B = (int)p.B; d.H = (int)p.H; d.N = p.N; d.M = (int)p.M; d.Mpad = p.Mpad;
   d.wg_per_bh = p.dec_wg_per_bh;

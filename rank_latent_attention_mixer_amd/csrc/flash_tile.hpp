@@ -238,6 +238,24 @@ struct FlashTile {
     }
     return __builtin_amdgcn_ballot_w64(bad) != 0ull;
   }
+
+  // The same test when every value row v is bounded, |v| <= vmax: the
+  // accumulators are sums of probabilities times values, so |o| <= l vmax
+  // and a row sum l with l vmax < 2^126 (and l >= kMinRowSum without a
+  // reference) implies finite accumulators.  With a reference the
+  // probabilities are at most 65504 (fp16) and the values fp16, so a finite
+  // l already bounds |o| far below the fp32 range.  NaN in l or vmax fails
+  // the comparisons and counts as overflow.
+  __device__ __forceinline__ bool overflowed_bounded(float vmax) const {
+    bool bad = false;
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      const float l = row_sum(cb);
+      if constexpr (REF) bad = bad || !__builtin_isfinite(l);
+      else bad = bad || !(l >= kMinRowSum) || !(l * vmax < 0x1p126f);
+    }
+    return __builtin_amdgcn_ballot_w64(bad) != 0ull;
+  }
 };
 
 }  // namespace flarepp

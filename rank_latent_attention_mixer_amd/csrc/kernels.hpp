@@ -70,6 +70,7 @@ struct DecodeParams {
   const void* k;          // [B, H, N, D]
   void* y;                // [B, H, N, D]
   float* lse_out;         // optional [B*H, N]: per token log2(row sum) + reference
+  unsigned long long* redo;  // per (workgroup, wave): tiles needing the exact path
   int B, H;
   int64_t N;
   int M, Mpad;
@@ -86,5 +87,6 @@ int encode_tile_tokens();                // tokens per encoder LDS tile
 int latent_pad(int M, int dtype);        // Mpad
 int decode_lds_bytes(int M, int D, int dtype);
 int decode_tokens_per_tile(int D);       // tokens per decoder workgroup iteration
+int decode_waves(int D);                 // waves per decoder workgroup
 
 }  // namespace flarepp

@@ -283,6 +283,29 @@ def test_decode_exact_recompute(fp, dtype, kind, amount):
     assert err <= TOL[dtype]
 
 
+def test_decode_accumulator_bound_triggers_exact_path(fp):
+    """bf16 decoder: row sums finite and in range (~2^100) but values near
+    2^30, so the accumulators (<= l max|z|) could pass the fp32 range; the
+    bound l max|z| < 2^126 sends these tokens to the exact path, whose
+    result is finite and matches the oracle."""
+    q, k, _ = _fallback_inputs("bf16", "shift", 49.0, decoder=True)
+    B, H, N, D = k.shape
+    M = q.shape[1]
+    rng = np.random.Generator(np.random.PCG64(6))
+    z = (rng.standard_normal((B, H, M, D)) * 2.0 ** 30).astype(np.float32)
+    s = 1.0 / math.sqrt(D)
+    note("[decode bound] bf16 shift 49, |z| ~ 2^30")
+    y = fp.flare_decode_fwd(torch.from_numpy(q).to(torch.bfloat16).cuda(), torch.from_numpy(z).cuda(),
+                            torch.from_numpy(k).to(torch.bfloat16).cuda(), s)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+    ref = oracle.decode_ref(q.astype(np.float64), z.astype(np.float64), k.astype(np.float64), s)
+    assert np.all(np.isfinite(y))
+    err = rel_err(y, ref)
+    note(f"[decode bound] rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------------------
 # Simplified FLARE++ (separate synthesis values, q = synthesized query)
 # ---------------------------------------------------------------------------
