@@ -329,6 +329,8 @@ def main(argv=None):
     ap.add_argument("--backward", action="store_true")
     ap.add_argument("--frontend", action="store_true")
     ap.add_argument("--probe", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="launch each timed forward as one replay of a captured HIP graph")
     a = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -378,13 +380,30 @@ def main(argv=None):
         fp.flarepp_mixer_fwd(*args, y=y, workspace=ws)
     torch.cuda.synchronize()
 
-    # the timed region: exactly K plain forwards
+    # the timed region: exactly K forwards (plain calls, or replays of one
+    # forward captured as a HIP graph)
+    graph = None
+    if a.graph:
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            fp.flarepp_mixer_fwd(*args, y=y, workspace=ws)
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fp.flarepp_mixer_fwd(*args, y=y, workspace=ws)
+        for _ in range(a.warmup):
+            graph.replay()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(a.steps):
-        fp.flarepp_mixer_fwd(*args, y=y, workspace=ws)
+        if graph is not None:
+            graph.replay()
+        else:
+            fp.flarepp_mixer_fwd(*args, y=y, workspace=ws)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -432,7 +451,7 @@ def main(argv=None):
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D,
                    "dtype": w.dtype, "global_batch": w.B, "seq_len": w.N,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "launch": "hip-graph" if a.graph else "stream"},
         "tflops": round(tflops, 2),
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
