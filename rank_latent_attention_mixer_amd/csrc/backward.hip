@@ -173,19 +173,22 @@ __device__ __forceinline__ void accumulate(f32x16 (&acc)[NDB], const V8 (&a)[NDB
   }
 }
 
-// Accumulator rows d = 32db + 8a + 4h + i of column lane%32, as float4 runs.
+// Accumulator rows d = 32db + 8a + 4h + i of column lane%32, as float4 runs;
+// with add set, added to what dst holds.
 template <int D, int NDB>
 __device__ __forceinline__ void store_acc_row(float* dst, const f32x16 (&acc)[NDB], int h,
-                                              float scale) {
+                                              float scale, int add = 0) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
       const int d0 = 32 * db + 8 * aa + 4 * h;
-      if (d0 < D)
-        *reinterpret_cast<f32x4*>(dst + d0) =
-            f32x4{acc[db][4 * aa] * scale, acc[db][4 * aa + 1] * scale,
-                  acc[db][4 * aa + 2] * scale, acc[db][4 * aa + 3] * scale};
+      if (d0 < D) {
+        f32x4 v = f32x4{acc[db][4 * aa] * scale, acc[db][4 * aa + 1] * scale,
+                        acc[db][4 * aa + 2] * scale, acc[db][4 * aa + 3] * scale};
+        if (add) v += *reinterpret_cast<const f32x4*>(dst + d0);
+        *reinterpret_cast<f32x4*>(dst + d0) = v;
+      }
     }
 }
 
@@ -394,8 +397,9 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
     }
     for (int m = tid; m < Mk; m += 64 * NWV) {
       const bool in = m < a.M;
-      vec[m] = in ? a.shift - a.lat_lse[(int64_t)set * a.M + m] : 0.f;
-      vec[Mk + m] = in ? a.lat_negd[(int64_t)set * a.M + m] : 0.f;
+      const int64_t i = (int64_t)set * (a.lat_stat_stride ? a.lat_stat_stride : a.M) + m;
+      vec[m] = in ? a.shift - a.lat_lse[i] : 0.f;
+      vec[Mk + m] = in ? a.lat_negd[i] : 0.f;
     }
   }
   __syncthreads();
@@ -418,7 +422,7 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
     float* out0 = a.out0 + ((int64_t)set * a.N + n) * D;
     float* out1 = a.out1 ? a.out1 + ((int64_t)set * a.N + n) * D : nullptr;
     if (closed) {  // the synthesis does not reach the output: zero gradient
-      if (n < a.N && h == 0)
+      if (n < a.N && h == 0 && !a.accumulate)
         for (int d = 0; d < D; d += 4) {
           *reinterpret_cast<f32x4*>(out0 + d) = f32x4{0.f, 0.f, 0.f, 0.f};
           if (out1) *reinterpret_cast<f32x4*>(out1 + d) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -476,14 +480,14 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
     if (n >= a.N) continue;
     const float up = exp2f(a.set_e[set]);
     if (out1) {
-      store_acc_row<D, NDB>(out0, y, h, up * a.s_over_c);
-      store_acc_row<D, NDB>(out1, x, h, up);
+      store_acc_row<D, NDB>(out0, y, h, up * a.s_over_c, a.accumulate);
+      store_acc_row<D, NDB>(out1, x, h, up, a.accumulate);
     } else {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) y[db][v] = fmaf(a.s_over_c, y[db][v], x[db][v]);
-      store_acc_row<D, NDB>(out0, y, h, up);
+      store_acc_row<D, NDB>(out0, y, h, up, a.accumulate);
     }
   }
 }
@@ -698,11 +702,41 @@ hipError_t tok_d(int D, const BwdTokParams& p, hipStream_t s) {
   }
 }
 
+// The token pass sums over latents, so a head whose latents do not fit one
+// workgroup's LDS runs as several launches over equal latent ranges (a
+// multiple of 32 each), the later ones adding into the gradients the first
+// one stored.
+template <int MODE, typename T>
+hipError_t tok_ranges(int D, const BwdTokParams& p, hipStream_t s) {
+  const int nr = bwd_tok_latent_ranges(p.M, D);
+  if (nr < 1) return hipErrorInvalidValue;
+  if (nr == 1) return tok_d<MODE, T>(D, p, s);
+  const int per = ((p.M + nr - 1) / nr + 31) & ~31;
+  for (int m0 = 0; m0 < p.M; m0 += per) {
+    BwdTokParams q = p;
+    q.M = p.M - m0 < per ? p.M - m0 : per;
+    q.lat_stat_stride = p.lat_stat_stride ? p.lat_stat_stride : p.M;
+    q.lat_lse = p.lat_lse + m0;
+    q.lat_negd = p.lat_negd + m0;
+    for (int t = 0; t < 3; ++t)
+      if (p.lat[t]) q.lat[t] = static_cast<const unsigned char*>(p.lat[t]) + (size_t)m0 * D * 2;
+    q.accumulate = p.accumulate || m0 > 0;
+    hipError_t e = tok_d<MODE, T>(D, q, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 int bwd_latents_per_block(int D) { return 32 * (D <= 32 ? lat_waves<32>() : lat_waves<64>()); }
 int bwd_tokens_per_tile() { return 32 * kBwdWaves; }
 size_t bwd_tok_lds_bytes(int M, int D) { return tok_lds(M, D); }
+int bwd_tok_latent_ranges(int M, int D) {
+  for (int nr = 1; nr <= M; ++nr)
+    if (tok_lds(((M + nr - 1) / nr + 31) & ~31, D) <= kBwdTokMaxLds) return nr;
+  return 0;
+}
 
 hipError_t launch_bwd_lat(int dtype, int mode, int D, const BwdLatParams& p, hipStream_t s) {
   const int lpb = bwd_latents_per_block(D);
@@ -719,11 +753,11 @@ hipError_t launch_bwd_lat(int dtype, int mode, int D, const BwdLatParams& p, hip
 
 hipError_t launch_bwd_tok(int dtype, int mode, int D, const BwdTokParams& p, hipStream_t s) {
   if (dtype == kBF16) {
-    if (mode == kBwdTokFlare) return tok_d<kBwdTokFlare, __bf16>(D, p, s);
-    return tok_d<kBwdTokSyn, __bf16>(D, p, s);
+    if (mode == kBwdTokFlare) return tok_ranges<kBwdTokFlare, __bf16>(D, p, s);
+    return tok_ranges<kBwdTokSyn, __bf16>(D, p, s);
   }
-  if (mode == kBwdTokFlare) return tok_d<kBwdTokFlare, _Float16>(D, p, s);
-  return tok_d<kBwdTokSyn, _Float16>(D, p, s);
+  if (mode == kBwdTokFlare) return tok_ranges<kBwdTokFlare, _Float16>(D, p, s);
+  return tok_ranges<kBwdTokSyn, _Float16>(D, p, s);
 }
 
 hipError_t launch_bwd_tok_prep(const BwdPrepParams& p, hipStream_t s) {

@@ -55,8 +55,9 @@ struct BwdLatParams {
 struct BwdTokParams {
   const void* lat[3];           // latent rows dtype: score/Y, G1 (flare), G2/X
   int64_t lat_b_stride[3], lat_h_stride[3];
-  const float* lat_lse;         // per-latent lse of P1 [sets][M]
-  const float* lat_negd;        // per-latent C of G2 [sets][M]
+  const float* lat_lse;         // per-latent lse of P1 [sets][lat_stat_stride]
+  const float* lat_negd;        // per-latent C of G2 [sets][lat_stat_stride]
+  int64_t lat_stat_stride;      // set stride of lat_lse / lat_negd (0: M)
   const void* kt;               // token score operand [B,H,N,D]
   const void* g1t;              // flare: token operand of G1 (dy)
   const void* g2t;              // token operand of G2 (v; synthesis: its values)
@@ -69,8 +70,9 @@ struct BwdTokParams {
   const float* gate;
   int B, H;
   int64_t N;
-  int M;
+  int M;                        // latents this launch covers
   int wg_per_bh;
+  int accumulate;               // add into out0/out1 instead of storing
 };
 
 // -Delta2 = -(dy . y) per token row.
@@ -144,5 +146,9 @@ hipError_t launch_bwd_norm(const BwdNormParams& p, hipStream_t s);
 int bwd_latents_per_block(int D);
 int bwd_tokens_per_tile();
 size_t bwd_tok_lds_bytes(int M, int D);
+// LDS one token-pass workgroup may hold (the CU's 160 KB).
+constexpr size_t kBwdTokMaxLds = 160 * 1024;
+// Launches over latent ranges the token pass takes for M latents (0: none fits).
+int bwd_tok_latent_ranges(int M, int D);
 
 }  // namespace flarepp

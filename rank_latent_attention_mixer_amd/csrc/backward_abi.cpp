@@ -30,7 +30,7 @@ int make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dty
   int st = check_shape(B, H, N, M, D, dtype);
   if (st != FLAREPP_OK) return st;
   if (dtype == FLAREPP_F32 || D < 16) return FLAREPP_ERR_UNSUPPORTED;  // matrix-core path only
-  if (bwd_tok_lds_bytes((int)M, (int)D) > 160 * 1024) return FLAREPP_ERR_UNSUPPORTED;
+  if (bwd_tok_latent_ranges((int)M, (int)D) < 1) return FLAREPP_ERR_UNSUPPORTED;
   p->B = B; p->H = H; p->N = N; p->M = M; p->D = D; p->dtype = dtype;
   p->Mpad = (int)((M + 31) / 32 * 32);
   const int64_t BH = B * H;

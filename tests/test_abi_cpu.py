@@ -181,7 +181,8 @@ def test_saved_size_formula():
     ((1, 8, 1 << 20, 512, 32, 1), True),
     ((2, 2, 700, 80, 16, 2), True),
     ((1, 1, 100, 416, 64, 1), True),
-    ((1, 1, 100, 448, 64, 1), False),    # latents of a head exceed the LDS
+    ((1, 1, 100, 512, 64, 2), True),     # token pass over two latent ranges
+    ((1, 1, 100, 513, 64, 1), False),    # M above the library's maximum
     ((1, 1, 100, 64, 8, 1), False),      # D = 8: no matrix-core backward
     ((1, 1, 100, 64, 32, 0), False),     # fp32
     ((1, 1, 0, 64, 32, 1), False),
@@ -213,7 +214,7 @@ def _bwd(B=1, H=2, N=1024, M=16, D=32, dt=1, saved_bytes=None, wsb=None, **kw):
     (dict(q0=None), INV), (dict(gate=None), INV), (dict(k0=None), INV), (dict(k=None), INV),
     (dict(y=None), INV), (dict(dy=None), INV), (dict(saved=None), INV), (dict(dq0=None), INV),
     (dict(dqf=None), INV), (dict(dgate=None), INV), (dict(dk0=None), INV), (dict(dk=None), INV),
-    (dict(dv=None), INV), (dict(D=8), UNS), (dict(dt=0), UNS), (dict(M=448, D=64), UNS),
+    (dict(dv=None), INV), (dict(D=8), UNS), (dict(dt=0), UNS), (dict(M=513), UNS),
     (dict(saved_bytes=64), WS), (dict(ws=None), WS), (dict(wsb=1), WS),
     (dict(dk="k"), INV), (dict(dv="dy"), INV), (dict(dk0="saved"), INV),
     (dict(dy=ctypes.c_void_p(0x10000000 * 27 + 8)), INV),       # misaligned dy

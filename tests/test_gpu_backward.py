@@ -94,6 +94,9 @@ SHAPES = [
     (1, 1, 37, 1, 32, "bf16", [0.5]),                      # a single latent
     (1, 2, 129, 512, 32, "bf16", [0.2, -0.7]),             # maximum M
     (3, 1, 128, 32, 32, "fp16", [0.1]),                    # exactly one tile
+    # D = 64 past the LDS of one token-pass workgroup: two latent ranges
+    (1, 2, 700, 512, 64, "bf16", [-np.inf, 0.5]),          # closed head too
+    (1, 1, 333, 450, 64, "fp16", [1.0]),                   # ranges 256 + 194
 ]
 
 
@@ -136,6 +139,7 @@ def test_single_token_closed_form(fp, dtype):
     (1, 3, 500, 40, 16, "fp16", 0.5),
     (1, 1, 2000, 256, 64, "bf16", 0.125),
     (1, 2, 7, 20, 32, "fp16", 1.0),
+    (1, 1, 1000, 512, 64, "bf16", 0.125),                  # two latent ranges
 ])
 def test_flare_bwd_vs_oracle(fp, B, H, N, M, D, dtype, scale):
     note(f"[bwd] flare B={B} H={H} N={N} M={M} D={D} {dtype} scale={scale}")
@@ -247,6 +251,7 @@ def test_fwd_train_output_equals_forward(fp):
     (1, 2, 1000, 64, 16, "fp16"),
     (1, 1, 513, 100, 64, "bf16"),
     (2, 1, 300, 33, 64, "fp16"),
+    (1, 1, 513, 480, 64, "bf16"),                          # two latent ranges
 ])
 def test_simplified_bwd_vs_oracle(fp, B, H, N, M, D, dtype):
     """Simplified mixer (separate synthesis values, q = q_dyn) against
