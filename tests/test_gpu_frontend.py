@@ -72,6 +72,11 @@ CASES = [
     (1, 513, 1024, 16, 64, "fp16", True, False),   # wide heads
     (3, 129, 32, 1, 64, "bf16", True, True),       # one head, F < one tile
     (1, 1, 16, 2, 16, "bf16", False, False),       # a single token
+    # resident-weight kernel (C a multiple of 64 up to 256)
+    (3, 50, 192, 4, 16, "fp16", True, True),       # C = 192; blocks straddle batches
+    (1, 700, 128, 6, 64, "bf16", True, True),      # F = 1152: last feature group half used
+    (2, 5, 256, 8, 32, "bf16", True, True),        # N < one block: one block over two batches
+    (1, 4097, 64, 1, 16, "fp16", False, False),    # F = 48, one wave; ragged last block
 ]
 
 
