@@ -403,15 +403,21 @@ __device__ __forceinline__ void wres_step(const FrontendParams& a, const WresWav
     return *reinterpret_cast<const V8*>(rowp + (k / P) * 32 * P +
                                         (((2 * (k % P) + s.h) ^ wr_swz<C>(s.r)) << 4));
   };
-  V8 x0 = rd(0), x1 = rd(1);
+  // (one step ahead only at D = 64, C = 256, whose epilogue needs the room)
+  constexpr int LA = (D == 64 && C == 256) ? 1 : 2;
+  V8 x0 = rd(0), x1 = LA > 1 ? rd(1) : x0;
 #pragma unroll
   for (int k = 0; k < KS; ++k) {
-    const V8 x2 = k + 2 < KS ? rd(k + 2) : x1;
+    const V8 x2 = k + LA < KS ? rd(k + LA) : x1;
     acc[0] = mfma_32x32x16(s.w[0][k], x0, acc[0]);
     acc[1] = mfma_32x32x16(s.w[1][k], x0, acc[1]);
     __builtin_amdgcn_sched_barrier(0);
-    x0 = x1;
-    x1 = x2;
+    if (LA > 1) {
+      x0 = x1;
+      x1 = x2;
+    } else {
+      x0 = x2;
+    }
   }
   // epilogue: the lane holds features fo + 32 fs + 8 aa + 4 h + i of token r
   if (s.any_norm) {

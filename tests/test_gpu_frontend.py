@@ -77,6 +77,7 @@ CASES = [
     (1, 700, 128, 6, 64, "bf16", True, True),      # F = 1152: last feature group half used
     (2, 5, 256, 8, 32, "bf16", True, True),        # N < one block: one block over two batches
     (1, 4097, 64, 1, 16, "fp16", False, False),    # F = 48, one wave; ragged last block
+    (2, 300, 256, 4, 64, "fp16", True, True),      # C = 256 at D = 64
 ]
 
 
