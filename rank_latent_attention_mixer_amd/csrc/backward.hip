@@ -33,6 +33,7 @@
 // T = P * G (= dS), and P.V-style products accumulating over the block's
 // keys with P or T as the B operand.
 #include <cmath>
+#include <type_traits>
 
 #include "backward.hpp"
 #include "flash_tile.hpp"
@@ -407,7 +408,6 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
   const unsigned char* lat1 = lds_raw + TB;
   const unsigned char* lat2 = lds_raw + 2 * TB;
   const int nfull = a.M / 32, mtail = a.M - 32 * nfull;
-  const int ngrp = nfull + (mtail > 0 ? 1 : 0);
 
   O ops;
   ops.init(lane);
@@ -444,7 +444,9 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
       y[db] = splat16(0.f);
       x[db] = splat16(0.f);
     }
-    for (int G = 0; G < ngrp; ++G) {
+    // one group of 32 latents; the masking of a partial last group is a
+    // compile-time variant, so full groups carry no selects
+    auto group = [&](int G, int kvalid, auto tail) {
       V8 lop[KD];
       ops.rows(lat0, G, lop);
       f32x16 s1 = product<V8, KD>(lop, kop, lds_rowvec(vec, G, h));
@@ -457,9 +459,9 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
         ops.rows(lat1, G, lop);
         g1 = product<V8, KD>(lop, b1, cg1);
       }
-      if (G == nfull) {
-        mask_slots(s1, mtail, h);
-        if constexpr (DEC) mask_slots(s2, mtail, h);
+      if constexpr (decltype(tail)::value) {
+        mask_slots(s1, kvalid, h);
+        if constexpr (DEC) mask_slots(s2, kvalid, h);
       }
       float p[16], t[16];
 #pragma unroll
@@ -476,6 +478,13 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
       accumulate<V8, NDB>(y, va, Tm);
       ops.cols(lat2, G, va);
       accumulate<V8, NDB>(x, va, P);
+    };
+    if constexpr (D == 64) {  // one code path (a second one spills at this width)
+      for (int G = 0; G * 32 < a.M; ++G) group(G, G < nfull ? 32 : mtail, std::true_type{});
+    } else {
+#pragma unroll 1
+      for (int G = 0; G < nfull; ++G) group(G, 32, std::false_type{});
+      if (mtail > 0) group(nfull, mtail, std::true_type{});
     }
     if (n >= a.N) continue;
     const float up = exp2f(a.set_e[set]);
