@@ -232,7 +232,7 @@ int flare_decode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
  *   dK = s dS^T Q.
  * The backward supports bf16 and fp16 with D in {16, 32, 64} and M <= 512
  * (the token pass holds a head's latents in one workgroup's 160 KiB LDS; at
- * D = 64 with M > 416 it runs over two latent ranges, the second adding into
+ * D = 64 with M > 384 it runs over two latent ranges, the second adding into
  * the gradients the first stored); other cases return
  * FLAREPP_ERR_UNSUPPORTED.  The token
  * tensors k, v, k0, y, dy and every gradient output (fp32) must be 16-byte

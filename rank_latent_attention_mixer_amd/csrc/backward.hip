@@ -381,7 +381,16 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
 
   const int Mk = (a.M + 31) & ~31;
   const int TB = Mk * L::ROWB;
-  float* vec = reinterpret_cast<float*>(lds_raw + 3 * TB);   // [2][Mk]
+  float* vec = reinterpret_cast<float*>(lds_raw + 3 * TB);   // [3][Mk]
+  // FLARE part, fast form: P2 = P1 U[m] W[n] with U = 2^(lse1 - shift - Ls)
+  // and W = 2^(Ls - lse2 - e) (the two weights share their score; Ls, the
+  // largest lse1 - shift of the range, keeps U <= 1), one exponential per
+  // pair instead of two.  Taken when W stays far inside fp32 for every token
+  // of the set (else the two-exponential form).
+  constexpr bool kFastForm = DEC && D <= 32;
+  __shared__ float red[2][16];
+  bool fast = false;
+  float Ls = 0.f;
   if (!closed) {
     // resident latents: rows [0, Mk) of each tensor, rows >= M zero
     const int CH = Mk * L::CPR;
@@ -396,11 +405,43 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
         *reinterpret_cast<u32x4*>(&lds_raw[t * TB + L::offset(row, 16 * c)]) = v;
       }
     }
+    float lmax = -__builtin_inff(), tmin = __builtin_inff();
     for (int m = tid; m < Mk; m += 64 * NWV) {
       const bool in = m < a.M;
       const int64_t i = (int64_t)set * (a.lat_stat_stride ? a.lat_stat_stride : a.M) + m;
       vec[m] = in ? a.shift - a.lat_lse[i] : 0.f;
       vec[Mk + m] = in ? a.lat_negd[i] : 0.f;
+      if (in) lmax = fmaxf(lmax, a.lat_lse[i]);
+    }
+    if constexpr (kFastForm) {
+      for (int p = tid; p < a.lse_min_parts; p += 64 * NWV)
+        tmin = fminf(tmin, a.tok_lse_min[(int64_t)set * a.lse_min_parts + p]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        lmax = fmaxf(lmax, __shfl_xor(lmax, o));
+        tmin = fminf(tmin, __shfl_xor(tmin, o));
+      }
+      if (lane == 0) {
+        red[0][wave] = lmax;
+        red[1][wave] = tmin;
+      }
+      __syncthreads();
+      lmax = red[0][0];
+      tmin = red[1][0];
+      for (int w = 1; w < NWV; ++w) {
+        lmax = fmaxf(lmax, red[0][w]);
+        tmin = fminf(tmin, red[1][w]);
+      }
+      Ls = lmax - a.shift;
+      // log2 of the largest W; the smallest is >= -17 - e (lse2 <= log2 M +
+      // the largest lse1), so bounding e bounds it too
+      const float e = a.set_e[set];
+      const float wmax = Ls - tmin - e;
+      fast = a.tok_lse_min != nullptr && fabsf(wmax) <= 100.f && fabsf(e) <= 100.f &&
+             fabsf(Ls) <= 1e30f;
+      if (fast)
+        for (int m = tid; m < Mk; m += 64 * NWV)
+          vec[2 * Mk + m] = m < a.M ? __builtin_amdgcn_exp2f(-vec[m] - Ls) : 0.f;
     }
   }
   __syncthreads();
@@ -433,9 +474,12 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
     load_row_op<V8, KD>(kg, nc, D, h, kop);
     load_row_op<V8, KD>(g2g, nc, D, h, b2);
     f32x16 cs2 = splat16(0.f), cg1 = splat16(0.f);
+    float wn = 0.f;
     if constexpr (DEC) {
       load_row_op<V8, KD>(g1g, nc, D, h, b1);
-      cs2 = splat16(-a.tok_lse[(int64_t)set * a.N + nc] - a.set_e[set]);
+      const float c2 = -a.tok_lse[(int64_t)set * a.N + nc] - a.set_e[set];
+      cs2 = splat16(c2);
+      wn = __builtin_amdgcn_exp2f(c2 + Ls);
       cg1 = splat16(a.tok_negd[(int64_t)set * a.N + nc]);
     }
     f32x16 y[NDB], x[NDB];
@@ -446,12 +490,13 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
     }
     // one group of 32 latents; the masking of a partial last group is a
     // compile-time variant, so full groups carry no selects
-    auto group = [&](int G, int kvalid, auto tail) {
+    auto group = [&](int G, int kvalid, auto tail, auto fast_form) {
+      constexpr bool FAST = decltype(fast_form)::value;
       V8 lop[KD];
       ops.rows(lat0, G, lop);
       f32x16 s1 = product<V8, KD>(lop, kop, lds_rowvec(vec, G, h));
       f32x16 s2 = splat16(0.f);
-      if constexpr (DEC) s2 = product<V8, KD>(lop, kop, cs2);
+      if constexpr (DEC && !FAST) s2 = product<V8, KD>(lop, kop, cs2);
       ops.rows(lat2, G, lop);
       const f32x16 g2 = product<V8, KD>(lop, b2, lds_rowvec(vec + Mk, G, h));
       f32x16 g1 = splat16(0.f);
@@ -461,14 +506,24 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
       }
       if constexpr (decltype(tail)::value) {
         mask_slots(s1, kvalid, h);
-        if constexpr (DEC) mask_slots(s2, kvalid, h);
+        if constexpr (DEC && !FAST) mask_slots(s2, kvalid, h);
       }
       float p[16], t[16];
+      if constexpr (FAST) {
+        // T = P1 (G2 + U W G1)
+        const f32x16 u = lds_rowvec(vec + 2 * Mk, G, h);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        p[v] = __builtin_amdgcn_exp2f(s1[v]);
-        t[v] = p[v] * g2[v];
-        if constexpr (DEC) t[v] = fmaf(__builtin_amdgcn_exp2f(s2[v]), g1[v], t[v]);
+        for (int v = 0; v < 16; ++v) {
+          p[v] = __builtin_amdgcn_exp2f(s1[v]);
+          t[v] = p[v] * fmaf(u[v], wn * g1[v], g2[v]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          p[v] = __builtin_amdgcn_exp2f(s1[v]);
+          t[v] = p[v] * g2[v];
+          if constexpr (DEC) t[v] = fmaf(__builtin_amdgcn_exp2f(s2[v]), g1[v], t[v]);
+        }
       }
       V8 Tm[2], P[2];
       pack16<T>(t, Tm);
@@ -480,11 +535,20 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
       accumulate<V8, NDB>(x, va, P);
     };
     if constexpr (D == 64) {  // one code path (a second one spills at this width)
-      for (int G = 0; G * 32 < a.M; ++G) group(G, G < nfull ? 32 : mtail, std::true_type{});
+      for (int G = 0; G * 32 < a.M; ++G)
+        group(G, G < nfull ? 32 : mtail, std::true_type{}, std::false_type{});
     } else {
+      auto groups = [&](auto fast_form) {
 #pragma unroll 1
-      for (int G = 0; G < nfull; ++G) group(G, 32, std::false_type{});
-      if (mtail > 0) group(nfull, mtail, std::true_type{});
+        for (int G = 0; G < nfull; ++G) group(G, 32, std::false_type{}, fast_form);
+        if (mtail > 0) group(nfull, mtail, std::true_type{}, fast_form);
+      };
+      if constexpr (kFastForm) {
+        if (fast) groups(std::true_type{});  // block-uniform
+        else groups(std::false_type{});
+      } else {
+        groups(std::false_type{});
+      }
     }
     if (n >= a.N) continue;
     const float up = exp2f(a.set_e[set]);
@@ -642,6 +706,23 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(BwdGateParams a) {
 // maximum (each of the set's workgroups reads it all, from L2) and writes
 // the rows [16 rb, 16 rb + 16).
 constexpr int kNormRows = 16;
+// Partial minima: block (set, p) reduces slice p of the set's N values.
+__global__ __launch_bounds__(256) void bwd_min_kernel(BwdMinParams a) {
+  const int set = blockIdx.x, p = blockIdx.y;
+  const int64_t per = (a.N + a.parts - 1) / a.parts;
+  const int64_t lo = (int64_t)p * per, hi = min(lo + per, a.N);
+  const float* v = a.vals + (int64_t)set * a.N;
+  float m = __builtin_inff();
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) m = fminf(m, v[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fminf(m, __shfl_xor(m, o));
+  __shared__ float w[4];
+  if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    a.part[(int64_t)set * a.parts + p] = fminf(fminf(w[0], w[1]), fminf(w[2], w[3]));
+}
+
 __global__ __launch_bounds__(256) void bwd_norm_kernel(BwdNormParams a) {
   const int set = blockIdx.x;
   const int m0 = blockIdx.y * kNormRows;
@@ -685,7 +766,7 @@ hipError_t lat_d(int D, const BwdLatParams& p, dim3 grid, hipStream_t s) {
 
 size_t tok_lds(int M, int D) {
   const size_t Mk = (size_t)((M + 31) & ~31);
-  return 3 * Mk * 2 * D + 2 * Mk * sizeof(float);
+  return 3 * Mk * 2 * D + 3 * Mk * sizeof(float);
 }
 
 template <int MODE, typename T, int D>
@@ -767,6 +848,11 @@ hipError_t launch_bwd_tok(int dtype, int mode, int D, const BwdTokParams& p, hip
   }
   if (mode == kBwdTokFlare) return tok_ranges<kBwdTokFlare, _Float16>(D, p, s);
   return tok_ranges<kBwdTokSyn, _Float16>(D, p, s);
+}
+
+hipError_t launch_bwd_min(const BwdMinParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_min_kernel, dim3((unsigned)p.sets, (unsigned)p.parts), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_tok_prep(const BwdPrepParams& p, hipStream_t s) {

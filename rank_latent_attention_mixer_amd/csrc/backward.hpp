@@ -73,6 +73,17 @@ struct BwdTokParams {
   int M;                        // latents this launch covers
   int wg_per_bh;
   int accumulate;               // add into out0/out1 instead of storing
+  const float* tok_lse_min;     // flare: [sets][lse_min_parts] partial minima of tok_lse
+  int lse_min_parts;
+};
+
+// Partial minima of a per-token row statistic: part[set][p] = min over the
+// p-th slice of the set's N values.
+struct BwdMinParams {
+  const float* vals;            // [sets][N]
+  float* part;                  // [sets][parts]
+  int64_t N;
+  int sets, parts;
 };
 
 // -Delta2 = -(dy . y) per token row.
@@ -143,11 +154,15 @@ hipError_t launch_bwd_dec_sums(const BwdSumsParams& p, hipStream_t s);
 hipError_t launch_bwd_add_sums(const BwdAddParams& p, hipStream_t s);
 hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s);
 hipError_t launch_bwd_norm(const BwdNormParams& p, hipStream_t s);
+hipError_t launch_bwd_min(const BwdMinParams& p, hipStream_t s);
+// Slices per set of the token-statistic minimum the FLARE token pass reads.
+constexpr int kBwdMinParts = 64;
 int bwd_latents_per_block(int D);
 int bwd_tokens_per_tile();
 size_t bwd_tok_lds_bytes(int M, int D);
-// LDS one token-pass workgroup may hold (the CU's 160 KB).
-constexpr size_t kBwdTokMaxLds = 160 * 1024;
+// Dynamic LDS one token-pass workgroup may hold (the CU's 160 KB, less
+// room for the kernel's small static reduction buffer).
+constexpr size_t kBwdTokMaxLds = 160 * 1024 - 512;
 // Launches over latent ranges the token pass takes for M latents (0: none fits).
 int bwd_tok_latent_ranges(int M, int D);
 

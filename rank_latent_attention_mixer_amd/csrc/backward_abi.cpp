@@ -23,7 +23,7 @@ struct BwdPlan {
   int dtype, Mpad, nchunks, mblocks, tok_wg_per_bh;
   int64_t chunk_tokens;
   size_t off_cq, off_zr, off_nd2, off_py, off_px, off_dq, off_dz, off_dzp, off_nd1, off_e1,
-      off_cq0, off_dqdp, off_nd0, off_e0, off_dq0s, total;
+      off_cq0, off_dqdp, off_nd0, off_e0, off_dq0s, off_l2min, total;
 };
 
 int make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, BwdPlan* p) {
@@ -69,6 +69,7 @@ int make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dty
   p->off_nd0 = take((size_t)BH * M * f);
   p->off_e0 = take((size_t)BH * f);
   p->off_dq0s = take((size_t)BH * M * D * f);
+  p->off_l2min = take((size_t)BH * kBwdMinParts * f);
   p->total = off;
   return FLAREPP_OK;
 }
@@ -192,6 +193,13 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   kp.out0 = dk; kp.out1 = dv; kp.s_over_c = scale / c; kp.shift = shift;
   kp.set_e = f32(p.off_e1);
   kp.B = (int)B; kp.H = (int)H; kp.N = N; kp.M = (int)M; kp.wg_per_bh = p.tok_wg_per_bh;
+  // per-set minimum of lse2 in slices: the range test of the token pass's
+  // one-exponential form
+  BwdMinParams mp;
+  mp.vals = sv.lse2; mp.part = f32(p.off_l2min); mp.N = N; mp.sets = (int)BH;
+  mp.parts = kBwdMinParts;
+  FLAREPP_TRY(launch_bwd_min(mp, s));
+  kp.tok_lse_min = f32(p.off_l2min); kp.lse_min_parts = kBwdMinParts;
   FLAREPP_TRY(launch_bwd_tok(dtype, kBwdTokFlare, (int)D, kp, s));
 
   // latent gradient summed over the batch; FLARE++: gate and synthesis operands

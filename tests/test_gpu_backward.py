@@ -159,6 +159,56 @@ def test_flare_bwd_vs_oracle(fp, B, H, N, M, D, dtype, scale):
         assert e <= TOL[dtype], (n, e)
 
 
+def test_flare_bwd_per_set_form_choice(fp):
+    """Head 0 has a token whose scores against every latent sit ~120 below the
+    rest (the token pass's one-exponential form would need a factor outside
+    fp32 there, so that set takes the two-exponential form); head 1 is
+    ordinary (one-exponential form).  The token pass's outputs dk, dv of both
+    heads against the oracle, and dq of the ordinary head (head 0's dq, from
+    the latent passes, carries the extreme token's key of norm 120 and
+    exceeds the bf16 bar for reasons unrelated to the form choice)."""
+    B, H, N, M, D, dtype = 1, 2, 300, 64, 32, "bf16"
+    scale = 1.0 / np.sqrt(D)
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((H, M, D)).astype(np.float32)
+    u = rng.standard_normal(D).astype(np.float32)
+    u = u / np.linalg.norm(u)
+    # head 0: latents 4u plus noise orthogonal to u; token 17 = -120 u scores
+    # about -122 (base 2) against every latent, the rest of order 1
+    w = 0.3 * rng.standard_normal((M, D)).astype(np.float32)
+    w -= np.outer(w @ u, u)
+    q[0] = 4.0 * u + w
+    k = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    k[0, 0, 17] = -120.0 * u
+    v = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    dy = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    rt = lambda a: torch.from_numpy(a).to(torch.bfloat16).float().numpy().astype(np.float64)
+    q64, k64, v64, dy64 = rt(q), rt(k), rt(v), rt(dy)
+    # the range that decides the form, from the definition (base-2 scores)
+    c = scale / np.log(2.0)
+    spread = []
+    for hh in range(H):
+        sc = c * q64[hh] @ k64[0, hh].T                       # [M, N]
+        lse1 = np.log2(np.sum(np.exp2(sc - sc.max(1, keepdims=True)), 1)) + sc.max(1)
+        lse2 = np.log2(np.sum(np.exp2(sc - sc.max(0, keepdims=True)), 0)) + sc.max(0)
+        spread.append(float(lse1.max() - lse2.min()))
+    note(f"[bwd] lse1 max - lse2 min per head: {spread}")
+    assert spread[0] > 110.0 and spread[1] < 60.0
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    y, saved = fp.flare_mixer_fwd_train(qd, kd, vd, scale)
+    g = fp.flare_mixer_bwd(qd, kd, vd, scale, y, dev(dy, dtype), saved)
+    torch.cuda.synchronize()
+    dq_ref, dk_ref, dv_ref = oracle.flare_bwd_ref(q64, k64, v64, scale, dy64)
+    for hh in range(H):
+        errs = {"dk": rel_err(g["dk"].cpu()[:, hh], dk_ref[:, hh]),
+                "dv": rel_err(g["dv"].cpu()[:, hh], dv_ref[:, hh])}
+        if hh == 1:
+            errs["dq"] = rel_err(g["dq"].cpu()[hh], dq_ref[hh])
+        note(f"[bwd] head {hh} " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= TOL[dtype], (hh, n, e)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_closed_gate_bwd_equals_flare_bitwise(fp, dtype):
     """With every gate closed FLARE++ is FLARE with q = q_fixed: the token
