@@ -156,7 +156,7 @@ hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s);
 hipError_t launch_bwd_norm(const BwdNormParams& p, hipStream_t s);
 hipError_t launch_bwd_min(const BwdMinParams& p, hipStream_t s);
 // Slices per set of the token-statistic minimum the FLARE token pass reads.
-constexpr int kBwdMinParts = 64;
+constexpr int kBwdMinParts = 256;
 int bwd_latents_per_block(int D);
 int bwd_tokens_per_tile();
 size_t bwd_tok_lds_bytes(int M, int D);
