@@ -69,13 +69,37 @@ def _link(objs, lib: str, verbose: bool) -> None:
     os.replace(tmp, lib)
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "flarepp_c_check.c")
+C_CHECK = os.path.join(ROOT, "tests", "c_abi", "flarepp_c_check")
+
+
+def _build_c_check(verbose: bool) -> None:
+    """The plain-C client the C-ABI test runs: gcc, the HIP runtime, and
+    libflarepp found next to the package through a relative rpath."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    tmp = C_CHECK + ".tmp"
+    cmd = [shutil.which("gcc") or "gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(rocm, "include"),
+           C_CHECK_SRC, "-o", tmp, "-L" + PKG, "-lflarepp", "-L" + os.path.join(rocm, "lib"),
+           "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/../../rank_latent_attention_mixer_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C client build failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, C_CHECK)
+
+
 def build(jobs: int = 4, verbose: bool = False) -> str:
-    """Builds libflarepp.so and the measurement probe libflarepp_probe.so."""
+    """Builds libflarepp.so, the measurement probe libflarepp_probe.so and
+    the plain-C client of the ABI (tests/c_abi)."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
     _link(objs[:len(SOURCES)], LIB, verbose)
     _link(objs[len(SOURCES):], PROBE_LIB, verbose)
+    _build_c_check(verbose)
     return LIB
 
 
