@@ -317,9 +317,14 @@ __global__ __launch_bounds__(64 * lat_waves<D>()) void bwd_lat_kernel(BwdLatPara
       V8 kop[KD];
       ops.rows(base, g, kop);
       f32x16 s = product<V8, KD>(kop, qop, DEC ? lds_rowvec(tvec[cur][0], g, h) : cs);
-      V8 gk[KD];
-      ops.rows(base + GI * TB, g, gk);
-      const f32x16 gg = product<V8, KD>(gk, gop, DEC ? lds_rowvec(tvec[cur][1], g, h) : cg);
+      f32x16 gg;
+      if constexpr (GI == 0) {  // synthesis: the G product's token rows are the score rows
+        gg = product<V8, KD>(kop, gop, cg);
+      } else {
+        V8 gk[KD];
+        ops.rows(base + GI * TB, g, gk);
+        gg = product<V8, KD>(gk, gop, DEC ? lds_rowvec(tvec[cur][1], g, h) : cg);
+      }
       if (kvalid < 32) mask_slots(s, kvalid, h);
       float p[16], t[16];
 #pragma unroll
