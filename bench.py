@@ -222,6 +222,12 @@ def bench_backward(a, fp, torch, np, w, x, args, y, ws):
                    "parallelism": "single-gpu", "pass": "backward"},
         "tflops": round(flops / t / 1e12, 2),
         "frac_bf16_peak": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+        # the whole backward pass against the matrix-core peak (its kernels
+        # are listed with their times in the backward kernel-time profile)
+        "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "whole backward", "algorithmic_flops_per_call": int(flops)},
         "source_digest": source_digest(),
     }
     print(json.dumps(result), flush=True)
