@@ -64,9 +64,9 @@ __device__ __forceinline__ float lse_state_base2(float m, float l) { return m + 
 // each of the four lanes of a slot merges every fourth chunk, then the
 // lanes combine in a fixed butterfly and the first lane writes.
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
-  const int set = blockIdx.y;
+  const int set = blockIdx.x;  // sets along x: their count may pass the y limit
   const int W4 = (a.out_kind == kOutValueT ? a.DV : a.D) / 4;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
   const int quarter = (int)(t & 3);
   const int64_t slot = t >> 2;
   const bool in_range = slot < (int64_t)a.Mpad * W4;  // all lanes stay for the shuffles
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   const int width = p.out_kind == kOutValueT ? p.DV : p.D;
   const int64_t n = (int64_t)p.Mpad * (width / 4) * 4;  // (latent, 4 columns, chunk quarter)
-  const dim3 grid((unsigned)((n + 255) / 256), (unsigned)p.nsets);
+  const dim3 grid((unsigned)p.nsets, (unsigned)((n + 255) / 256));
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -369,9 +369,11 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams a) {
   __shared__ float qsm[TM][D];
   __shared__ float zsm[TM][D];
   const int tid = threadIdx.x;
-  const int bh = blockIdx.y;
+  // one-dimensional grid of ceil(N / 256) blocks per (b, h), heads outermost
+  const int64_t bpb = (a.N + 255) / 256;
+  const int bh = (int)(blockIdx.x / bpb);
   const int b = bh / a.H, h = bh - b * a.H;
-  const int64_t n = (int64_t)blockIdx.x * blockDim.x + tid;
+  const int64_t n = ((int64_t)blockIdx.x - (int64_t)bh * bpb) * 256 + tid;
   const bool valid = n < a.N;
   const float* kb = reinterpret_cast<const float*>(a.k) + (int64_t)bh * a.N * D;
   const float* qb = reinterpret_cast<const float*>(a.q) + b * a.q_b_stride + h * a.q_h_stride;
@@ -456,7 +458,9 @@ hipError_t launch_mfma_d(int D, const DecodeParams& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_f32(const DecodeParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)((p.N + 255) / 256), (unsigned)(p.B * p.H));
+  const int64_t blocks = (p.N + 255) / 256 * p.B * p.H;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
   hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }

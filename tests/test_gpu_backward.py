@@ -97,6 +97,7 @@ SHAPES = [
     # D = 64 past the LDS of one token-pass workgroup: two latent ranges
     (1, 2, 700, 512, 64, "bf16", [-np.inf, 0.5]),          # closed head too
     (1, 1, 333, 450, 64, "fp16", [1.0]),                   # ranges 256 + 194
+    (4, 32, 9, 24, 16, "bf16", list(np.linspace(-2.0, 2.0, 32))),  # 128 heads
 ]
 
 

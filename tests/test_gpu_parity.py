@@ -123,6 +123,8 @@ EDGE = [
     (1, 1, 257, 96, 16, "bf16"),     # two encoder tiles plus one token
     (3, 1, 128, 32, 32, "fp16"),     # exactly one encoder tile
     (1, 1, 2000, 512, 64, "bf16"),   # wide heads at maximum M
+    (8, 64, 5, 16, 32, "bf16"),      # 512 heads of a few tokens each
+    (4, 32, 70, 512, 16, "fp16"),    # 128 heads at maximum M
 ]
 
 
@@ -134,6 +136,25 @@ def test_edge_shapes(fp, B, H, N, M, D, dtype):
     err = rel_err(y, oracle.flarepp_ref(**f64(x)))
     note(f"[edge] rel err {err:.3e}")
     assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_head_count_past_grid_y_limit(fp, dtype):
+    """67,584 (b, h) pairs, more than a grid's y extent holds: every launch
+    keeps the head index on x. Whole batches sampled at the start, middle
+    and end are checked against the oracle."""
+    B, H, N, M, D = 2048, 33, 3, 5, 8
+    note(f"[heads] B{B} H{H} N{N} M{M} D{D} {dtype}")
+    x = make_random_inputs(B, H, N, M, D, dtype, seed=4242)
+    y = run_mixer(fp, x, dtype)
+    assert np.all(np.isfinite(y))
+    for b in (0, B // 2 - 1, B - 1):
+        xb = dict(x)
+        for n in ("k0", "k", "v"):
+            xb[n] = x[n][b:b + 1]
+        err = rel_err(y[b:b + 1], oracle.flarepp_ref(**f64(xb)))
+        note(f"[heads] batch {b} rel err {err:.3e}")
+        assert err <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
