@@ -193,6 +193,34 @@ __device__ __forceinline__ void store_acc_row(float* dst, const f32x16 (&acc)[ND
     }
 }
 
+// Dot product of two 16-byte chunks of 8 operand values: four two-term dot
+// instructions, fp32 accumulation (each product of two 16-bit values is
+// exact in fp32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, int dtype) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // elements copied out first: a bit cast of a vector element expression
+    // itself reads the vector's first element whatever the index
+    const unsigned x = a[j], y = b[j];
+    acc = dtype == kBF16
+              ? __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                                __builtin_bit_cast(bf16x2_t, y), acc, false)
+              : __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, x),
+                                       __builtin_bit_cast(f16x2_t, y), acc, false);
+  }
+  return acc;
+}
+
+// v plus the value of lane ^ 1 (and, with x2, of lane ^ 2) within each quad.
+__device__ __forceinline__ float quad_xor_add(float v, bool x2) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+  if (x2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Latents in registers, tokens streamed through LDS.
 // ---------------------------------------------------------------------------
@@ -204,6 +232,12 @@ constexpr int kBwdTile = 128;  // tokens per LDS tile
 // latents), 8 at D = 64.
 template <int D>
 constexpr int lat_waves() { return D <= 32 ? 16 : 8; }
+
+// Whether the decoder's latent pass forms -Delta2 itself: its tile staging
+// (one 16-byte chunk per thread) leaves at least as many threads idle as
+// it uses.
+template <int D>
+constexpr bool lat_forms_delta2() { return 2 * kBwdTile * RowLayout<D>::CPR <= 64 * lat_waves<D>(); }
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(64 * lat_waves<D>()) void bwd_lat_kernel(BwdLatParams a) {
@@ -264,8 +298,20 @@ __global__ __launch_bounds__(64 * lat_waves<D>()) void bwd_lat_kernel(BwdLatPara
   // rows past the chunk's end repeat its last token (their weights are 0)
   constexpr int CH = kBwdTile * L::CPR;                      // chunks per tensor per tile
   constexpr int PER = (CH + 64 * NWV - 1) / (64 * NWV);
+  // Decoder: where the tile's chunks leave whole waves idle (threads CH to
+  // 2 CH - 1), those waves stage the tile's dy chunks a second time with the
+  // matching y chunks and form -Delta2 = -(dy . y) per token, for this
+  // pass's G product and, stored, for the token pass.
+  constexpr bool kDelta = lat_forms_delta2<D>() && DEC;
+  constexpr int kDt = std::is_same<T, __bf16>::value ? kBF16 : kF16;
+  const int e2 = tid - CH;
+  const bool delta_lane = kDelta && e2 >= 0 && e2 < CH;     // wave-uniform
+  const unsigned char* ybase =
+      kDelta ? reinterpret_cast<const unsigned char*>(a.y_tok) + ((int64_t)set * a.N + n0) * D * 2
+             : nullptr;
   u32x4 stage[NT][PER];
   float sv0 = 0.f, sv1 = 0.f;
+  float lmin = __builtin_inff();  // decoder: minimum lse2 over the chunk's tokens
   auto fetch = [&](int tile) {
     const int lim = ntok - 1 - tile * kBwdTile;
 #pragma unroll
@@ -281,10 +327,19 @@ __global__ __launch_bounds__(64 * lat_waves<D>()) void bwd_lat_kernel(BwdLatPara
     if (DEC && tid < kBwdTile) {
       const int64_t n = (int64_t)set * a.N + n0 + tile * kBwdTile + min(tid, lim);
       sv0 = a.tok_lse[n];
-      sv1 = a.tok_negd[n];
+      lmin = fminf(lmin, sv0);
+      if constexpr (!kDelta) sv1 = a.tok_negd[n];
+    }
+    if constexpr (kDelta) {
+      if (delta_lane) {
+        const int row = e2 / L::CPR, c = e2 - row * L::CPR;
+        const int64_t off = ((int64_t)(tile * kBwdTile + min(row, lim)) * D + 8 * c) * 2;
+        stage[0][0] = ldg16(tbase[1] + off);  // dy
+        stage[1][0] = ldg16(ybase + off);     // y
+      }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, int tile) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -295,15 +350,29 @@ __global__ __launch_bounds__(64 * lat_waves<D>()) void bwd_lat_kernel(BwdLatPara
           *reinterpret_cast<u32x4*>(&lds[buf][t * TB + L::offset(row, 16 * c)]) = stage[t][i];
         }
       }
+    if constexpr (kDelta) {
+      if (delta_lane) {
+        // the same chunk products and lane butterfly as the separate
+        // per-token pass, so -Delta2 comes out bit for bit the same
+        static_assert(L::CPR == 2 || L::CPR == 4, "one row per lane quad");
+        const float v = quad_xor_add(dot8(stage[0][0], stage[1][0], kDt), L::CPR == 4);
+        const int row = e2 / L::CPR;
+        if (e2 - row * L::CPR == 0) {
+          tvec[buf][1][row] = -v;
+          if (blockIdx.y == 0 && tile * kBwdTile + row < ntok)
+            a.negd_out[(int64_t)set * a.N + n0 + tile * kBwdTile + row] = -v;
+        }
+      }
+    }
     if (DEC && tid < kBwdTile) {
       tvec[buf][0][tid] = -sv0;
-      tvec[buf][1][tid] = sv1;
+      if constexpr (!kDelta) tvec[buf][1][tid] = sv1;
     }
   };
 
   if (ntiles > 0) {
     fetch(0);
-    store(0);
+    store(0, 0);
   }
   __syncthreads();
   for (int tile = 0; tile < ntiles; ++tile) {
@@ -344,10 +413,19 @@ __global__ __launch_bounds__(64 * lat_waves<D>()) void bwd_lat_kernel(BwdLatPara
         accumulate<V8, NDB>(x, va, P);
       }
     }
-    if (tile + 1 < ntiles) store(cur ^ 1);
+    if (tile + 1 < ntiles) store(cur ^ 1, tile + 1);
     __syncthreads();
   }
 
+  if constexpr (DEC) {
+    // two partial minima per chunk (the two waves that read lse2), for the
+    // token pass's choice of its one-exponential form
+    if (a.lse_min_out != nullptr && blockIdx.y == 0 && wave < kBwdTile / 64) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) lmin = fminf(lmin, __shfl_xor(lmin, o));
+      if (lane == 0) a.lse_min_out[((int64_t)set * a.nchunks + chunk) * 2 + wave] = lmin;
+    }
+  }
   if (col >= a.M) return;
   const int64_t prow = ((int64_t)set * a.nchunks + chunk) * a.Mpad + col;
   store_acc_row<D, NDB>(a.part[0] + prow * D, y, h, 1.f);
@@ -592,27 +670,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Dot product of two 16-byte chunks of 8 operand values.
-__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, int dtype) {
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const unsigned ua = (a[j] >> (16 * half)) & 0xFFFFu, ub = (b[j] >> (16 * half)) & 0xFFFFu;
-      float fa, fb;
-      if (dtype == kBF16) {
-        fa = __uint_as_float(ua << 16);
-        fb = __uint_as_float(ub << 16);
-      } else {
-        fa = (float)__builtin_bit_cast(_Float16, (unsigned short)ua);
-        fb = (float)__builtin_bit_cast(_Float16, (unsigned short)ub);
-      }
-      acc = fmaf(fa, fb, acc);
-    }
-  return acc;
-}
-
 // -Delta2 = -(dy . y) per token row: D/8 lanes per row, one 16-byte chunk
 // each, reduced over the row's lanes.
 __global__ __launch_bounds__(256) void bwd_tok_prep_kernel(BwdPrepParams a) {
@@ -711,22 +768,6 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(BwdGateParams a) {
 // maximum (each of the set's workgroups reads it all, from L2) and writes
 // the rows [16 rb, 16 rb + 16).
 constexpr int kNormRows = 16;
-// Partial minima: block (set, p) reduces slice p of the set's N values.
-__global__ __launch_bounds__(256) void bwd_min_kernel(BwdMinParams a) {
-  const int set = blockIdx.x, p = blockIdx.y;
-  const int64_t per = (a.N + a.parts - 1) / a.parts;
-  const int64_t lo = (int64_t)p * per, hi = min(lo + per, a.N);
-  const float* v = a.vals + (int64_t)set * a.N;
-  float m = __builtin_inff();
-  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) m = fminf(m, v[i]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fminf(m, __shfl_xor(m, o));
-  __shared__ float w[4];
-  if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    a.part[(int64_t)set * a.parts + p] = fminf(fminf(w[0], w[1]), fminf(w[2], w[3]));
-}
 
 __global__ __launch_bounds__(256) void bwd_norm_kernel(BwdNormParams a) {
   const int set = blockIdx.x;
@@ -824,6 +865,9 @@ hipError_t tok_ranges(int D, const BwdTokParams& p, hipStream_t s) {
 
 }  // namespace
 
+bool bwd_lat_forms_delta2(int D) {
+  return D == 16 ? lat_forms_delta2<16>() : D == 32 ? lat_forms_delta2<32>() : lat_forms_delta2<64>();
+}
 int bwd_latents_per_block(int D) { return 32 * (D <= 32 ? lat_waves<32>() : lat_waves<64>()); }
 int bwd_tokens_per_tile() { return 32 * kBwdWaves; }
 size_t bwd_tok_lds_bytes(int M, int D) { return tok_lds(M, D); }
@@ -855,10 +899,6 @@ hipError_t launch_bwd_tok(int dtype, int mode, int D, const BwdTokParams& p, hip
   return tok_ranges<kBwdTokSyn, _Float16>(D, p, s);
 }
 
-hipError_t launch_bwd_min(const BwdMinParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_min_kernel, dim3((unsigned)p.sets, (unsigned)p.parts), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_tok_prep(const BwdPrepParams& p, hipStream_t s) {
   const int64_t n = p.rows * (p.D / 8);

@@ -35,7 +35,10 @@ struct BwdLatParams {
   const float* lse;             // Enc/Syn: per-latent lse [sets][M]
   const float* negg;            // Enc/Syn: per-latent C of G [sets][M]
   const float* tok_lse;         // Dec: per-token lse2 [sets][N]
-  const float* tok_negd;        // Dec: per-token -Delta2 [sets][N]
+  const float* tok_negd;        // Dec: per-token -Delta2 [sets][N] (read unless formed here)
+  const void* y_tok;            // Dec, where the pass forms -Delta2: y [B,H,N,D] dtype
+  float* negd_out;              // ... and where it stores it [sets][N]
+  float* lse_min_out;           // Dec, optional: partial minima of lse2 [sets][nchunks][2]
   const void* t[2];             // token tensors [B,H,N,D] dtype: score rows / Y, G rows / X
   float* part[2];               // [sets][nchunks][Mpad][D]: Y, X
   int B, H;
@@ -75,15 +78,6 @@ struct BwdTokParams {
   int accumulate;               // add into out0/out1 instead of storing
   const float* tok_lse_min;     // flare: [sets][lse_min_parts] partial minima of tok_lse
   int lse_min_parts;
-};
-
-// Partial minima of a per-token row statistic: part[set][p] = min over the
-// p-th slice of the set's N values.
-struct BwdMinParams {
-  const float* vals;            // [sets][N]
-  float* part;                  // [sets][parts]
-  int64_t N;
-  int sets, parts;
 };
 
 // -Delta2 = -(dy . y) per token row.
@@ -154,10 +148,10 @@ hipError_t launch_bwd_dec_sums(const BwdSumsParams& p, hipStream_t s);
 hipError_t launch_bwd_add_sums(const BwdAddParams& p, hipStream_t s);
 hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s);
 hipError_t launch_bwd_norm(const BwdNormParams& p, hipStream_t s);
-hipError_t launch_bwd_min(const BwdMinParams& p, hipStream_t s);
-// Slices per set of the token-statistic minimum the FLARE token pass reads.
-constexpr int kBwdMinParts = 256;
 int bwd_latents_per_block(int D);
+// Whether the decoder's latent pass forms -Delta2 itself (then no separate
+// per-token pass runs before it).
+bool bwd_lat_forms_delta2(int D);
 int bwd_tokens_per_tile();
 size_t bwd_tok_lds_bytes(int M, int D);
 // Dynamic LDS one token-pass workgroup may hold (the CU's 160 KB, less

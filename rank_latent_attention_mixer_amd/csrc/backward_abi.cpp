@@ -69,7 +69,7 @@ int make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dty
   p->off_nd0 = take((size_t)BH * M * f);
   p->off_e0 = take((size_t)BH * f);
   p->off_dq0s = take((size_t)BH * M * D * f);
-  p->off_l2min = take((size_t)BH * kBwdMinParts * f);
+  p->off_l2min = take((size_t)BH * p->nchunks * 2 * f);
   p->total = off;
   return FLAREPP_OK;
 }
@@ -142,11 +142,15 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   rp.out = at(p.off_zr); rp.scale = 1.f;
   FLAREPP_TRY(launch_bwd_rows(rp, s));
 
-  // -Delta2 per token
-  BwdPrepParams tp;
-  tp.dy = dy; tp.y = y; tp.negd = f32(p.off_nd2);
-  tp.rows = BH * N; tp.D = (int)D; tp.dtype = dtype;
-  FLAREPP_TRY(launch_bwd_tok_prep(tp, s));
+  // -Delta2 per token: formed inside the decoder's latent pass where its
+  // tile staging leaves threads free, else by a pass of its own
+  const bool lat_delta = bwd_lat_forms_delta2((int)D);
+  if (!lat_delta) {
+    BwdPrepParams tp;
+    tp.dy = dy; tp.y = y; tp.negd = f32(p.off_nd2);
+    tp.rows = BH * N; tp.D = (int)D; tp.dtype = dtype;
+    FLAREPP_TRY(launch_bwd_tok_prep(tp, s));
+  }
 
   // decoder, sums over tokens: dz = A2^T dy, dq = s dS2^T k
   BwdLatParams lp;
@@ -154,6 +158,8 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   lp.qop = at(p.off_cq); lp.q_b_stride = H * rowH; lp.q_h_stride = rowH;
   lp.gop = at(p.off_zr);
   lp.tok_lse = sv.lse2; lp.tok_negd = f32(p.off_nd2);
+  lp.y_tok = lat_delta ? y : nullptr; lp.negd_out = lat_delta ? f32(p.off_nd2) : nullptr;
+  lp.lse_min_out = f32(p.off_l2min);
   lp.t[0] = k; lp.t[1] = dy;
   lp.part[0] = f32(p.off_py); lp.part[1] = f32(p.off_px);
   lp.B = (int)B; lp.H = (int)H; lp.N = N; lp.M = (int)M; lp.Mpad = p.Mpad;
@@ -174,7 +180,8 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   // encoder, sums over tokens: dq += s dS1 k
   lp.gop = at(p.off_dzp);
   lp.lse = sv.lse1; lp.negg = f32(p.off_nd1);
-  lp.tok_lse = nullptr; lp.tok_negd = nullptr;
+  lp.tok_lse = nullptr; lp.tok_negd = nullptr; lp.y_tok = nullptr; lp.negd_out = nullptr;
+  lp.lse_min_out = nullptr;
   lp.t[1] = v;
   FLAREPP_TRY(launch_bwd_lat(dtype, kBwdLatEnc, (int)D, lp, s));
   BwdAddParams ap;
@@ -193,13 +200,9 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   kp.out0 = dk; kp.out1 = dv; kp.s_over_c = scale / c; kp.shift = shift;
   kp.set_e = f32(p.off_e1);
   kp.B = (int)B; kp.H = (int)H; kp.N = N; kp.M = (int)M; kp.wg_per_bh = p.tok_wg_per_bh;
-  // per-set minimum of lse2 in slices: the range test of the token pass's
-  // one-exponential form
-  BwdMinParams mp;
-  mp.vals = sv.lse2; mp.part = f32(p.off_l2min); mp.N = N; mp.sets = (int)BH;
-  mp.parts = kBwdMinParts;
-  FLAREPP_TRY(launch_bwd_min(mp, s));
-  kp.tok_lse_min = f32(p.off_l2min); kp.lse_min_parts = kBwdMinParts;
+  // partial minima of lse2 per set, from the decoder's latent pass: the
+  // range test of the token pass's one-exponential form
+  kp.tok_lse_min = f32(p.off_l2min); kp.lse_min_parts = 2 * p.nchunks;
   FLAREPP_TRY(launch_bwd_tok(dtype, kBwdTokFlare, (int)D, kp, s));
 
   // latent gradient summed over the batch; FLARE++: gate and synthesis operands
