@@ -702,59 +702,79 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdRowsParams a) {
   st_op(a.out, i, a.dtype, v);
 }
 
+// Four lanes per output: lane q of a slot sums the chunks c = q mod 4, then
+// the four combine in a fixed butterfly (every lane stays for the shuffles).
+__device__ __forceinline__ float chunk_sum4(const float* part, int64_t stride, int nchunks, int q) {
+  float acc = 0.f;
+#pragma unroll 4
+  for (int c = q; c < nchunks; c += 4) acc += part[(int64_t)c * stride];
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  return acc;
+}
+
 // After the decoder's latent pass: dq = s Y, dz = X, summed over chunks.
 __global__ __launch_bounds__(256) void bwd_dec_sums_kernel(BwdSumsParams a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)a.sets * a.M * a.D) return;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int q = (int)(t & 3);
+  const int64_t total = (int64_t)a.sets * a.M * a.D;
+  const int64_t i = min(t >> 2, total - 1);
   const int64_t set = i / ((int64_t)a.M * a.D);
   const int64_t md = i - set * a.M * a.D;
   const int m = (int)(md / a.D), d = (int)(md - (int64_t)m * a.D);
-  float X = 0.f, Y = 0.f;
-  for (int c = 0; c < a.nchunks; ++c) {
-    const int64_t p = (((int64_t)set * a.nchunks + c) * a.Mpad + m) * a.D + d;
-    Y += a.part[0][p];
-    X += a.part[1][p];
+  const int64_t p = (((int64_t)set * a.nchunks) * a.Mpad + m) * a.D + d;
+  const int64_t stride = (int64_t)a.Mpad * a.D;
+  const float Y = chunk_sum4(a.part[0] + p, stride, a.nchunks, q);
+  const float X = chunk_sum4(a.part[1] + p, stride, a.nchunks, q);
+  if (q == 0 && (t >> 2) < total) {
+    a.dq[i] = a.s * Y;
+    a.dz[i] = X;
   }
-  a.dq[i] = a.s * Y;
-  a.dz[i] = X;
 }
 
 // dst (+)= s 2^e * (sum over chunks of a latent pass's Y), per (set, m, d).
 __global__ __launch_bounds__(256) void bwd_add_sums_kernel(BwdAddParams a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)a.sets * a.M * a.D) return;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int q = (int)(t & 3);
+  const int64_t total = (int64_t)a.sets * a.M * a.D;
+  const int64_t i = min(t >> 2, total - 1);
   const int64_t set = i / ((int64_t)a.M * a.D);
   const int64_t md = i - set * a.M * a.D;
   const int m = (int)(md / a.D), d = (int)(md - (int64_t)m * a.D);
-  float acc = 0.f;
-  for (int c = 0; c < a.nchunks; ++c)
-    acc += a.part[(((int64_t)set * a.nchunks + c) * a.Mpad + m) * a.D + d];
-  const float f = a.s * (a.set_e ? exp2f(a.set_e[set]) : 1.f);
-  a.dst[i] = a.accumulate ? a.dst[i] + f * acc : f * acc;
+  const float acc = chunk_sum4(a.part + (((int64_t)set * a.nchunks) * a.Mpad + m) * a.D + d,
+                               (int64_t)a.Mpad * a.D, a.nchunks, q);
+  if (q == 0 && (t >> 2) < total) {
+    const float f = a.s * (a.set_e ? exp2f(a.set_e[set]) : 1.f);
+    a.dst[i] = a.accumulate ? a.dst[i] + f * acc : f * acc;
+  }
 }
 
 // Per head: latent gradient summed over the batch and the gate gradient.
-// One workgroup per head, fixed reduction order.
+// One workgroup per head (1024 threads, four loads in flight each), fixed
+// reduction order.
+constexpr int kGateThreads = 1024;
 //   dqf = sum_b dq;  dgate = sigma (1 - sigma) sum_{b,m,d} dq q_dyn
-__global__ __launch_bounds__(256) void bwd_gate_kernel(BwdGateParams a) {
+__global__ __launch_bounds__(kGateThreads) void bwd_gate_kernel(BwdGateParams a) {
   const int hd = blockIdx.x;
   const int tid = threadIdx.x;
-  __shared__ float red[256];
-  for (int md = tid; md < a.M * a.D; md += 256) {
+  __shared__ float red[kGateThreads];
+  const int MD = a.M * a.D;
+#pragma unroll 4
+  for (int md = tid; md < MD; md += kGateThreads) {
     float acc = 0.f;
     for (int b = 0; b < a.B; ++b) acc += a.dq[((int64_t)(b * a.H + hd) * a.M) * a.D + md];
-    if (a.dqf) a.dqf[(int64_t)hd * a.M * a.D + md] = acc;
+    if (a.dqf) a.dqf[(int64_t)hd * MD + md] = acc;
   }
   if (!a.synthesis) return;
   float part = 0.f;
-  for (int b = 0; b < a.B; ++b)
-    for (int md = tid; md < a.M * a.D; md += 256) {
-      const int64_t i = ((int64_t)(b * a.H + hd) * a.M) * a.D + md;
-      part += a.dq[i] * a.qd[i];
-    }
+  for (int b = 0; b < a.B; ++b) {
+    const int64_t base = ((int64_t)(b * a.H + hd) * a.M) * a.D;
+#pragma unroll 4
+    for (int md = tid; md < MD; md += kGateThreads) part += a.dq[base + md] * a.qd[base + md];
+  }
   red[tid] = part;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
+  for (int o = kGateThreads / 2; o > 0; o >>= 1) {
     if (tid < o) red[tid] += red[tid + o];
     __syncthreads();
   }
@@ -911,7 +931,7 @@ hipError_t launch_bwd_rows(const BwdRowsParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_bwd_dec_sums(const BwdSumsParams& p, hipStream_t s) {
-  const int64_t n = (int64_t)p.sets * p.M * p.D;
+  const int64_t n = (int64_t)p.sets * p.M * p.D * 4;
   hipLaunchKernelGGL(bwd_dec_sums_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -921,12 +941,12 @@ hipError_t launch_bwd_norm(const BwdNormParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_bwd_add_sums(const BwdAddParams& p, hipStream_t s) {
-  const int64_t n = (int64_t)p.sets * p.M * p.D;
+  const int64_t n = (int64_t)p.sets * p.M * p.D * 4;
   hipLaunchKernelGGL(bwd_add_sums_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 hipError_t launch_bwd_gate(const BwdGateParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)p.H), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)p.H), dim3(kGateThreads), 0, s, p);
   return hipGetLastError();
 }
 
