@@ -798,7 +798,13 @@ __global__ __launch_bounds__(256) void bwd_norm_kernel(BwdNormParams a) {
   const float* w = a.w + (int64_t)set * a.M * a.D;
   __shared__ float red[256];
   float mx = 0.f;
-  for (int md = tid; md < a.M * a.D; md += 256) mx = fmaxf(mx, fabsf(alpha * src[md]));
+  const f32x4* src4 = reinterpret_cast<const f32x4*>(src);  // M D is a multiple of 4
+#pragma unroll 4
+  for (int i = tid; i < a.M * a.D / 4; i += 256) {
+    const f32x4 v = src4[i];
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(alpha * v[0]), fabsf(alpha * v[1])),
+                         fmaxf(fabsf(alpha * v[2]), fabsf(alpha * v[3]))));
+  }
   red[tid] = mx;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
