@@ -23,6 +23,8 @@
 // of one token tile run on one XCD and share its L2 copy of x.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "flarepp_device.hpp"
 #include "frontend.hpp"
 #include "kernels.hpp"
@@ -262,6 +264,11 @@ void frontend_kernel(FrontendParams a) {
 // nothing.  The workgroups of the feature groups of one token range are
 // numbered onto one XCD so they share its L2 copy of x.
 constexpr int kWrFeat = 256;         // features per workgroup
+// Workgroup numbering: nnorm feature groups (the first ones, which hold
+// normalised features) and rx token ranges per XCD for every group.
+struct WresSplit {
+  int nnorm, rx;
+};
 constexpr int kWrTok = 32;           // tokens per block
 constexpr int kWrBufs = 3;
 constexpr int kWrStageB = 32 * 128;  // 32 tokens x 64 features x 2 B
@@ -461,7 +468,7 @@ __device__ __forceinline__ void wres_step(const FrontendParams& a, const WresWav
 
 template <typename T, int D, int C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void frontend_wres_kernel(FrontendParams a, int ranges_per_xcd) {
+void frontend_wres_kernel(FrontendParams a, WresSplit sp) {
   typedef typename Pack8<T>::type V8;
   using S = WresWave<T, D, C>;
   constexpr int KS = S::KS, QE = S::QE;
@@ -481,10 +488,17 @@ void frontend_wres_kernel(FrontendParams a, int ranges_per_xcd) {
   const int FG = (s.Fi + kWrFeat - 1) / kWrFeat;
   const int g = blockIdx.x;
   const int xcd = g % kXcds, slot = g / kXcds;
-  const int fg = slot % FG;
-  const int range = (slot / FG) * kXcds + xcd;
+  // the feature groups that normalise (the first sp.nnorm) cost ~1.3x a
+  // plain group per block and take the first slots of every XCD, the plain
+  // groups the rest; the plain groups of one token range sit side by side
+  const int nplain = FG - sp.nnorm;
+  const bool norm_slot = slot < sp.nnorm * sp.rx;
+  const int t = norm_slot ? slot : slot - sp.nnorm * sp.rx;
+  const int ncls = norm_slot ? sp.nnorm : nplain;
+  const int fg = norm_slot ? t % ncls : sp.nnorm + t % ncls;
+  const int range = (t / ncls) * kXcds + xcd;
   const int64_t nblk = (a.T + kWrTok - 1) / kWrTok;
-  const int64_t R = (int64_t)kXcds * ranges_per_xcd;
+  const int64_t R = (int64_t)kXcds * sp.rx;
   const int64_t per = (nblk + R - 1) / R;
   const int64_t b0 = range * per;
   const int64_t nb = min(b0 + per, nblk) - b0;
@@ -588,10 +602,15 @@ template <typename T, int D, int C>
 hipError_t wres_launch(const FrontendParams& p, hipStream_t s) {
   const int F = 3 * p.H * D;
   const int FG = (F + kWrFeat - 1) / kWrFeat;
-  // about two resident workgroups per CU (256 CUs)
-  int rpx = 512 / (kXcds * FG);
-  if (rpx < 1) rpx = 1;
-  const int64_t G = (int64_t)kXcds * FG * rpx;
+  // about two resident workgroups per CU (256 CUs).  The normalising groups
+  // (sum of squares, reciprocal root and two multiplies per value) are the
+  // slowest; numbered first, they measured 0.719 -> 0.693 ms at the
+  // million-token width, against 0.70-0.71 ms for giving them more, shorter
+  // ranges in proportion to their cost.
+  WresSplit sp;
+  sp.nnorm = p.normalize ? std::min(FG, (p.H * D + kWrFeat - 1) / kWrFeat) : 0;
+  sp.rx = std::max(1, 512 / (kXcds * FG));
+  const int64_t G = (int64_t)kXcds * FG * sp.rx;
   if (G > 0x7FFFFFFF) return hipErrorInvalidValue;
   const size_t lds = wres_lds_bytes(C);
   if (lds > 64 * 1024) {
@@ -599,7 +618,7 @@ hipError_t wres_launch(const FrontendParams& p, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((frontend_wres_kernel<T, D, C>), dim3((unsigned)G), dim3(256), lds, s, p, rpx);
+  hipLaunchKernelGGL((frontend_wres_kernel<T, D, C>), dim3((unsigned)G), dim3(256), lds, s, p, sp);
   return hipGetLastError();
 }
 
