@@ -89,9 +89,24 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(path, workload, kernel):
+FRONTEND_SOURCES = ("frontend.hip", "frontend.hpp", "frontend_abi.cpp", "flarepp_device.hpp",
+                    "kernels.hpp", "abi_common.hpp")
+
+
+def frontend_digest() -> str:
+    """Digest of the front end's kernel sources and the headers they include."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_latent_attention_mixer_amd", "csrc")
+    for f in FRONTEND_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path, workload, kernel, digest=None):
     """HBM bytes per launch of `kernel` from a counter summary made of lines
-    'key value...'; None unless it was taken on the current kernel sources."""
+    'key value...'; None unless it was taken on the current kernel sources
+    (`digest`, by default the forward's)."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -100,7 +115,7 @@ def read_traffic(path, workload, kernel):
             f = line.split()
             if len(f) >= 2 and not line.startswith("#"):
                 kv[f[0]] = f[1:]
-    if kv.get("source_digest", [None])[0] != source_digest():
+    if kv.get("source_digest", [None])[0] != (digest or source_digest()):
         return None
     if kv.get("workload", [None])[0] != workload:
         return None
@@ -315,8 +330,12 @@ def bench_frontend(a, fp, torch, w):
                    "dtype": w.dtype, "pass": "frontend"},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": nbytes},
+                     "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": read_traffic(os.path.join(ROOT, "profiles",
+                                                          f"hbm_traffic_frontend_{w.name}.txt"),
+                                             w.name, "frontend_wres", frontend_digest()),
+                     "kernel": "frontend_wres", "algorithmic_bytes_per_launch": nbytes},
+        "source_digest": frontend_digest(),
         "tflops": round(flops / t / 1e12, 2),
     }
     print(json.dumps(result), flush=True)
