@@ -78,3 +78,20 @@ def test_modes_need_a_device(args):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args,
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and r.stdout == ""
+
+
+def test_frontend_traffic_follows_the_front_end_sources(tmp_path):
+    """The committed front-end counter summary is read while the front end's
+    sources are the ones it was taken on, and a summary carrying another
+    digest (sources changed since) reads as None."""
+    committed = os.path.join(ROOT, "profiles", "hbm_traffic_frontend_million_token_bf16.txt")
+    d = bench.frontend_digest()
+    assert d != bench.source_digest()
+    got = bench.read_traffic(committed, "million_token_bf16", "frontend_wres", d)
+    if f"source_digest {d}\n" in open(committed).read():
+        assert got is not None and got > 2147876864  # at least the algorithmic bytes
+    else:  # sources edited since the counters were taken
+        assert got is None
+    stale = tmp_path / "t.txt"
+    stale.write_text(open(committed).read().replace(f"source_digest {d}", "source_digest 0000000000000000"))
+    assert bench.read_traffic(str(stale), "million_token_bf16", "frontend_wres", d) is None
