@@ -38,7 +38,10 @@ reason in the design notes of the repository):
 * no mask: every query attends to every key.
 
 Pinned by tests/test_oracle_pins.py (closed forms, invariants, brute force,
-hand-worked golden cases and an independent library attention routine).
+hand-worked golden cases and an independent library attention routine) and,
+function by function, by tests/test_oracle_units.py (every public function
+here against torch's fp64 attention or autograd, scalar brute force or a
+closed form, including latents given per batch element).
 """
 
 from __future__ import annotations
@@ -47,7 +50,6 @@ import numpy as np
 
 __all__ = [
     "gate_sigma",
-    "softmax_rows",
     "attention",
     "attention_matrix",
     "encode_ref",
@@ -76,14 +78,6 @@ def gate_sigma(g):
     g = _f64(g)
     with np.errstate(over="ignore"):
         return 1.0 / (1.0 + np.exp(-g))
-
-
-def softmax_rows(L):
-    """Row-wise softmax of a 2-D score matrix: subtract the row maximum,
-    exponentiate, divide by the row sum.  Returns a new array."""
-    L = _f64(L)
-    E = np.exp(L - L.max(axis=-1, keepdims=True))
-    return E / E.sum(axis=-1, keepdims=True)
 
 
 def attention_matrix(qh, kh, scale):
