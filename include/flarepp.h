@@ -27,6 +27,13 @@
  *   Token tensors are [B, H, N, D]; latent tensors [H, M, D] are shared by
  *   all batch elements.  Element type is given by `dtype` (flarepp_dtype);
  *   the gate is always fp32.
+ * - Alignment: every token, latent, output and saved-tensor pointer must be
+ *   16-byte aligned (the kernels move them in 16-byte vectors); the
+ *   workspace needs 256 bytes.  A misaligned pointer is
+ *   FLAREPP_ERR_INVALID_ARGUMENT (workspace: FLAREPP_ERR_WORKSPACE).
+ * - Aliasing: outputs (y, z, saved tensors, gradients) and the workspace are
+ *   written by the kernels; none of them may overlap each other or any
+ *   input, else FLAREPP_ERR_INVALID_ARGUMENT.
  * - Arithmetic: products accumulate in fp32; softmax statistics are fp32;
  *   intermediates q, z are kept in fp32 and rounded to the input dtype only
  *   where they feed a matrix-core product.  The output is rounded to the
@@ -68,7 +75,8 @@ typedef enum {
   FLAREPP_OK = 0,
   FLAREPP_ERR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, overflow, bad dtype,
                                        non-finite or non-positive scale, output
-                                       aliasing an input */
+                                       or workspace aliasing an input, pointer
+                                       not 16-byte aligned */
   FLAREPP_ERR_UNSUPPORTED = 2,      /* D not in {8,16,32,64}, M > 512, or the
                                        current device is not gfx950 */
   FLAREPP_ERR_WORKSPACE = 3,        /* workspace NULL, too small or not 256-byte

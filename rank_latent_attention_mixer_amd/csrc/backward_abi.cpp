@@ -107,11 +107,13 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   const size_t toke = (size_t)(B * H * N * D) * 2, late = (size_t)(H * M * D) * 2;
   if (ws == nullptr || ws_bytes < p.total || ((uintptr_t)ws % kAlign) != 0)
     return FLAREPP_ERR_WORKSPACE;
+  // the workspace is written by the kernels, so it counts as an output
   if (outputs_alias({{dq0, pp ? latf : 0}, {dq_lat, latf}, {dgate, dgate ? (size_t)H * 4 : 0},
-                     {dk0, pp ? tokf : 0}, {dv0, simplified ? tokf : 0}, {dk, tokf}, {dv, tokf}},
+                     {dk0, pp ? tokf : 0}, {dv0, simplified ? tokf : 0}, {dk, tokf}, {dv, tokf},
+                     {ws, ws_bytes}},
                     {{q0, late}, {gate, gate ? (size_t)H * 4 : 0}, {k0, toke}, {v0, toke},
                      {q_flare, late}, {k, toke}, {v, toke}, {y, toke}, {dy, toke},
-                     {saved, sv.floats * 4}, {ws, ws_bytes}}))
+                     {saved, sv.floats * 4}}))
     return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_device()) != FLAREPP_OK) return st;
 

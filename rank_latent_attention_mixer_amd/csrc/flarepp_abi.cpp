@@ -187,6 +187,9 @@ int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
                void* const* events, float* saved = nullptr, size_t saved_bytes = 0) {
   const bool simplified = q_fixed == nullptr && gate == nullptr;
   if (!q0 || !k0 || !v0 || !k || !v || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q0) || !aligned16(k0) || !aligned16(v0) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(y) || (q_fixed && !aligned16(q_fixed)))
+    return FLAREPP_ERR_INVALID_ARGUMENT;
   Plan p;
   int st = make_plan(B, H, N, M, D, dtype, 0, &p);
   if (st != FLAREPP_OK) return st;
@@ -201,9 +204,9 @@ int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   if (saved && (saved_bytes < sv.floats * sizeof(float) ||
                 (reinterpret_cast<uintptr_t>(saved) & 15)))
     return FLAREPP_ERR_WORKSPACE;
-  if (outputs_alias({{y, tok}, {saved, saved ? sv.floats * 4 : 0}},
+  if (outputs_alias({{y, tok}, {saved, saved ? sv.floats * 4 : 0}, {ws, ws_bytes}},
                     {{q0, lat}, {q_fixed, lat}, {gate, gate ? (size_t)H * 4 : 0}, {k0, tok},
-                     {v0, tok}, {k, tok}, {v, tok}, {ws, ws_bytes}}))
+                     {v0, tok}, {k, tok}, {v, tok}}))
     return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_device()) != FLAREPP_OK) return st;
 
@@ -259,6 +262,8 @@ int flare_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
                const void* q, const void* k, const void* v, void* y, void* ws, size_t ws_bytes,
                void* stream, float* saved = nullptr, size_t saved_bytes = 0) {
   if (!q || !k || !v || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y))
+    return FLAREPP_ERR_INVALID_ARGUMENT;
   Plan p;
   int st = make_plan(B, H, N, M, D, dtype, 0, &p);
   if (st != FLAREPP_OK) return st;
@@ -272,8 +277,8 @@ int flare_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   if (saved && (saved_bytes < sv.floats * sizeof(float) ||
                 (reinterpret_cast<uintptr_t>(saved) & 15)))
     return FLAREPP_ERR_WORKSPACE;
-  if (outputs_alias({{y, tok}, {saved, saved ? sv.floats * 4 : 0}},
-                    {{q, lat}, {k, tok}, {v, tok}, {ws, ws_bytes}}))
+  if (outputs_alias({{y, tok}, {saved, saved ? sv.floats * 4 : 0}, {ws, ws_bytes}},
+                    {{q, lat}, {k, tok}, {v, tok}}))
     return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_device()) != FLAREPP_OK) return st;
 
@@ -384,6 +389,8 @@ int flare_encode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
                      size_t workspace_bytes, void* stream) {
   try {
     if (!q || !k || !v || !z) return FLAREPP_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z))
+      return FLAREPP_ERR_INVALID_ARGUMENT;
     Plan p;
     int st = make_plan(B, H, N, M, D, dtype, chunk_tokens, &p);
     if (st != FLAREPP_OK) return st;
@@ -395,7 +402,8 @@ int flare_encode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
     if (overlaps(z, zb, k, tok) || overlaps(z, zb, v, tok) || overlaps(z, zb, q, lat))
       return FLAREPP_ERR_INVALID_ARGUMENT;
     if ((st = check_workspace(p, workspace, workspace_bytes)) != FLAREPP_OK) return st;
-    if (overlaps(z, zb, workspace, workspace_bytes)) return FLAREPP_ERR_INVALID_ARGUMENT;
+    if (outputs_alias({{z, zb}, {workspace, workspace_bytes}}, {{q, lat}, {k, tok}, {v, tok}}))
+      return FLAREPP_ERR_INVALID_ARGUMENT;
     if ((st = check_device()) != FLAREPP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float c = (float)((double)scale * 1.4426950408889634);
@@ -421,6 +429,8 @@ int flare_decode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
                      void* stream) {
   try {
     if (!q || !z || !k || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(z) || !aligned16(k) || !aligned16(y))
+      return FLAREPP_ERR_INVALID_ARGUMENT;
     Plan p;
     int st = make_plan(B, H, N, M, D, dtype, 0, &p);
     if (st != FLAREPP_OK) return st;
@@ -432,7 +442,8 @@ int flare_decode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
     if (overlaps(y, tok, k, tok) || overlaps(y, tok, z, zb) || overlaps(y, tok, q, lat))
       return FLAREPP_ERR_INVALID_ARGUMENT;
     if ((st = check_workspace(p, workspace, workspace_bytes)) != FLAREPP_OK) return st;
-    if (overlaps(y, tok, workspace, workspace_bytes)) return FLAREPP_ERR_INVALID_ARGUMENT;
+    if (outputs_alias({{y, tok}, {workspace, workspace_bytes}}, {{q, lat}, {z, zb}, {k, tok}}))
+      return FLAREPP_ERR_INVALID_ARGUMENT;
     if ((st = check_device()) != FLAREPP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float c = (float)((double)scale * 1.4426950408889634);

@@ -95,6 +95,10 @@ def _mixer(B=1, H=2, N=1024, M=16, D=8, dt=1, q0="q0", qf="qf", gate="gate", k0=
     (dict(y="k"), INV), (dict(y="v"), INV), (dict(y="k0"), INV), (dict(y="q0"), INV),
     (dict(y=ctypes.c_void_p(0x10000000 * 5 + 8)), INV),         # y overlaps k
     (dict(y="ws"), INV),                                         # y overlaps the workspace
+    (dict(k="ws"), INV), (dict(q0="ws"), INV),                   # an input overlaps the workspace
+    (dict(k=ctypes.c_void_p(0x10000000 * 5 + 8)), INV),          # misaligned k
+    (dict(y=ctypes.c_void_p(0x10000000 * 7 + 2)), INV),          # misaligned y
+    (dict(qf=ctypes.c_void_p(0x10000000 * 2 + 4)), INV),         # misaligned q_fixed
 ])
 def test_mixer_rejects_before_any_launch(kw, code):
     assert _mixer(**kw) == code
@@ -133,6 +137,22 @@ def test_encode_and_decode_seams_validate():
                               FAKE["k"], FAKE["ws"], wsd, None) == INV
     assert L.flare_decode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 0, None, FAKE["k"],
                               FAKE["y"], FAKE["ws"], wsd, None) == INV
+    # inputs overlapping the workspace (which the kernels write) and misaligned pointers
+    assert L.flare_encode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 0, FAKE["ws"], FAKE["v"],
+                              FAKE["z"], 64, FAKE["ws"], ws, None) == INV
+    assert L.flare_encode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 0, FAKE["k"], FAKE["v"],
+                              ctypes.c_void_p(FAKE["z"].value + 4), 64, FAKE["ws"], ws, None) == INV
+    assert L.flare_decode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["ws"], 0, FAKE["z"], FAKE["k"],
+                              FAKE["y"], FAKE["ws"], wsd, None) == INV
+    assert L.flare_decode_fwd(2, 2, 128, 16, 8, 1, 0.5, FAKE["q0"], 0, FAKE["z"],
+                              ctypes.c_void_p(FAKE["k"].value + 8), FAKE["y"], FAKE["ws"], wsd,
+                              None) == INV
+    ws_flare = fp.flarepp_workspace_size(1, 2, 64, 16, 8, 1)
+    assert L.flare_mixer_fwd(1, 2, 64, 16, 8, 1, 0.5, FAKE["q0"], FAKE["ws"], FAKE["v"],
+                             FAKE["y"], FAKE["ws"], ws_flare, None) == INV
+    assert L.flare_mixer_fwd(1, 2, 64, 16, 8, 1, 0.5, FAKE["q0"], FAKE["k"],
+                             ctypes.c_void_p(FAKE["v"].value + 2), FAKE["y"], FAKE["ws"],
+                             ws_flare, None) == INV
 
 
 def _simplified(B=1, H=2, N=1024, M=16, D=8, dt=1, q0="q0", k0="k0", v0="v0", k="k", v="v",
@@ -220,6 +240,7 @@ def _bwd(B=1, H=2, N=1024, M=16, D=32, dt=1, saved_bytes=None, wsb=None, **kw):
     (dict(dy=ctypes.c_void_p(0x10000000 * 27 + 8)), INV),       # misaligned dy
     (dict(dk=ctypes.c_void_p(0x10000000 * 24 + 4)), INV),       # misaligned dk
     (dict(dk="bws"), INV),                                        # gradient over the workspace
+    (dict(k="bws"), INV), (dict(saved="bws"), INV),               # input over the workspace
     (dict(dq0="dk"), INV), (dict(dgate="dq0"), INV), (dict(dv="dk0"), INV),  # gradients alias
     (dict(dqf="q0"), INV),                                        # latent gradient over an input
 ])
