@@ -37,6 +37,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "FLARE++ mixer fwd tokens/s & TFLOP/s (%bf16 MFMA peak), 1 GPU, N=1M M=512"
+
+# The pages' own statement of scale, restated (context, not a target).
+# FLARE.py README, section "FLARE" ("Scale" bullet): two-step FLARE trains end
+# to end on meshes of about one million points on one GPU; physicsnemo issue
+# #1150, opening description (one million tokens on a single GPU) and reply
+# item 3 (that study used mixed precision, fp16 forward and fp32 backward).
+# No GPU model is named for this claim on the pages.
+PAGES_CONTEXT = {
+    "claim": "FLARE (two-step, not FLARE++) trained end to end at about 1e6 tokens on a single GPU",
+    "hardware": "not named by the pages",
+    "precision": "mixed: fp16 forward, fp32 backward",
+    "throughput": "none printed by the pages",
+    "source": ('FLARE.py README, section "FLARE" (Scale bullet); physicsnemo issue #1150, '
+               "opening description and reply item 3"),
+    "role": "context, not a target",
+}
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 KERNELS = ["prep_seeds", "encode_synthesis", "combine_query", "encode", "combine_value",
@@ -482,6 +498,7 @@ def main(argv=None):
         "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
         "roofline": roofline,
         "cpu_baseline": None,
+        "context": PAGES_CONTEXT,
         "source_digest": source_digest(),
     }
     if not a.no_cpu_baseline:

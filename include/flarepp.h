@@ -322,10 +322,11 @@ int simplified_flarepp_mixer_bwd(int64_t B, int64_t H, int64_t N, int64_t M, int
                                  size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * Front end of the block (FLARE.py README, "FLARE++": three input
+ * Front end of the block (issue #2024, "Changes from v1 to v2": three input
  * projections, the synthesis keys and values shared; the synthesis call
  * normalised head by head -- its exact form is in the paper's Appendix A,
- * which the pages do not include).  Reading taken: a projection is
+ * which the pages do not include; the core mixer of the FLARE.py README,
+ * section "FLARE++", has neither projections nor normalisation).  Reading taken: a projection is
  * x @ W^T + b with W in the [H*D, C] layout of a linear layer, split into H
  * heads of D features (head-major); the head-wise normalisation is
  * u / sqrt(mean_d(u_d^2) + eps) * g over the D features of one head, applied

@@ -5,12 +5,14 @@ TEST INFRASTRUCTURE, NOT PRODUCT CODE (same rules as flarepp_oracle.py).
 
 What the pages state:
 
-* FLARE.py README, section "FLARE++", list of design changes: FLARE++ uses
-  three input projections instead of four (the synthesis keys and values are
-  shared, so one C -> C projection is saved), and it normalises the
-  synthesis call head by head: the seeds and the synthesis keys/values.
-  The core-mixer listing takes k0, k, v as key/value projections of the
-  input, [B, H, N, D].
+* Issue #2024, "[FEA]: Update FLARE++ to the v2 reference design ...",
+  section "Changes from v1 to v2": FLARE++ uses three input projections
+  instead of four (the synthesis keys and values are shared, so one C -> C
+  projection is saved), and it normalises the synthesis call head by head:
+  the seeds and the synthesis keys/values.
+* FLARE.py README, section "FLARE++": the core mixer itself has no
+  projections or normalisation; its listing takes k0, k, v already
+  projected, [B, H, N, D].
 * The exact form of the normalisation is in the paper's Appendix A, which is
   not on the pages.
 

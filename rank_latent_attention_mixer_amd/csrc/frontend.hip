@@ -1,8 +1,8 @@
 // Front end of the FLARE++ block on the gfx950 matrix cores: the three
 // input projections k0, k, v of the token features and the head-wise
-// normalisation of k0 (FLARE.py README, "FLARE++": three projections, the
-// synthesis keys and values shared; the synthesis call normalised head by
-// head), and the same normalisation of the seeds q0.
+// normalisation of k0 (issue #2024, "Changes from v1 to v2": three
+// projections, the synthesis keys and values shared; the synthesis call
+// normalised head by head), and the same normalisation of the seeds q0.
 //
 // One launch computes all three projections as one GEMM over the
 // concatenated output features F = 3 H D:  out[t][j] = x[t] . W_p[r] + b_p[r]

@@ -95,3 +95,16 @@ def test_frontend_traffic_follows_the_front_end_sources(tmp_path):
     stale = tmp_path / "t.txt"
     stale.write_text(open(committed).read().replace(f"source_digest {d}", "source_digest 0000000000000000"))
     assert bench.read_traffic(str(stale), "million_token_bf16", "frontend_wres", d) is None
+
+
+def test_bench_line_carries_the_pages_context_claim():
+    """The result line quotes the pages' scale claim as context, with the
+    hardware the pages name for it (none) and no target attached."""
+    import bench
+    src = open(bench.__file__).read()
+    assert '"context": PAGES_CONTEXT' in src
+    c = bench.PAGES_CONTEXT
+    assert "1e6 tokens on a single GPU" in c["claim"] and "FLARE" in c["claim"]
+    assert c["hardware"] == "not named by the pages"
+    assert c["role"] == "context, not a target"
+    assert "#1150" in c["source"] and "FLARE.py README" in c["source"]
