@@ -127,6 +127,28 @@ int flarepp_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * flarepp_mixer_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The call allocates nothing; its
+ * kernels use a device array owned by the library, FLAREPP_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per device, held from the first such call on a device until the
+ * process ends.  Every call on one device shares that array: calls that
+ * overlap in time on one device (two streams, or two host threads) race and
+ * must be serialised by the caller.  The kernels need no part of the array
+ * cleared between calls.
+ *   Arguments and results as for flarepp_mixer_fwd (same kernels, same
+ *   token chunking, so the same bits).
+ *   FLAREPP_ERR_WORKSPACE: flarepp_workspace_size(B,H,N,M,D,dtype) exceeds
+ *   FLAREPP_NOALLOC_SCRATCH_BYTES (checked before any HIP call); use
+ *   flarepp_mixer_fwd with a caller workspace for such shapes.
+ */
+#define FLAREPP_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int flarepp_mixer_fwd_noalloc(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
+                              const void* q0, const void* q_fixed, const float* gate,
+                              const void* k0, const void* k, const void* v, void* y,
+                              void* stream);
+
+/*
  * Same computation as flarepp_mixer_fwd, with timing marks for profiling.
  * `events` points to FLAREPP_TIMED_EVENTS hipEvent_t handles created by the
  * caller; the call records them on `stream` around its launches:

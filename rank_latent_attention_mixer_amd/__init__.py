@@ -9,6 +9,8 @@ library is missing, loading it raises.
 Entry points (same names as the C ABI in include/flarepp.h):
 
 * ``flarepp_mixer_fwd(q0, q_fixed, gate, k0, k, v)`` -> y
+* ``flarepp_mixer_fwd_noalloc(q0, q_fixed, gate, k0, k, v, y)`` -> y (no workspace;
+  the library's own per-device array of FLAREPP_NOALLOC_SCRATCH_BYTES)
 * ``simplified_flarepp_mixer_fwd(q0, k0, v0, k, v)`` -> y
 * ``flare_mixer_fwd(q, k, v, scale)`` -> y
 * ``flarepp_mixer_fwd_train(...)`` -> (y, saved); ``flarepp_mixer_bwd(..., y, dy, saved)``
@@ -27,7 +29,8 @@ import re
 
 __all__ = [
     "FlareppError", "load_library", "library_path", "dtype_code",
-    "flarepp_mixer_fwd", "flarepp_mixer_fwd_timed", "simplified_flarepp_mixer_fwd",
+    "flarepp_mixer_fwd", "flarepp_mixer_fwd_noalloc", "flarepp_mixer_fwd_timed",
+    "simplified_flarepp_mixer_fwd", "FLAREPP_NOALLOC_SCRATCH_BYTES",
     "flare_mixer_fwd", "flare_encode_fwd", "flare_decode_fwd",
     "flarepp_mixer_fwd_train", "flarepp_mixer_bwd", "flare_mixer_fwd_train", "flare_mixer_bwd",
     "simplified_flarepp_mixer_fwd_train", "simplified_flarepp_mixer_bwd",
@@ -47,6 +50,7 @@ FLAREPP_ERR_UNSUPPORTED = 2
 FLAREPP_ERR_WORKSPACE = 3
 FLAREPP_ERR_HIP = 4
 FLAREPP_F32, FLAREPP_BF16, FLAREPP_F16 = 0, 1, 2
+FLAREPP_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 _lib = None
 
@@ -87,6 +91,8 @@ def load_library():
     lib.flare_decode_workspace_size.restype = sz
     lib.flarepp_mixer_fwd.argtypes = shape + [i32] + [vp] * 7 + [vp, sz, vp]
     lib.flarepp_mixer_fwd.restype = i32
+    lib.flarepp_mixer_fwd_noalloc.argtypes = shape + [i32] + [vp] * 7 + [vp]
+    lib.flarepp_mixer_fwd_noalloc.restype = i32
     lib.flarepp_mixer_fwd_timed.argtypes = shape + [i32] + [vp] * 7 + [vp, sz, vp, vp]
     lib.flarepp_mixer_fwd_timed.restype = i32
     lib.simplified_flarepp_mixer_fwd.argtypes = shape + [i32] + [vp] * 6 + [vp, sz, vp]
@@ -222,6 +228,26 @@ def flarepp_mixer_fwd(q0, q_fixed, gate, k0, k, v, y=None, workspace=None, strea
     _call(lib.flarepp_mixer_fwd, "flarepp_mixer_fwd", B, H, N, M, D, code, _ptr(q0),
           _ptr(q_fixed), _ptr(gate), _ptr(k0), _ptr(k), _ptr(v), _ptr(y), _ptr(ws),
           ws.numel(), _stream(stream))
+    return y
+
+
+def flarepp_mixer_fwd_noalloc(q0, q_fixed, gate, k0, k, v, y, stream=None):
+    """FLARE++ mixer forward with no workspace argument (the library's own
+    per-device array; the C call allocates nothing); see include/flarepp.h.
+    y must be given.  Returns y."""
+    import torch
+    lib = load_library()
+    B, H, N, D = k.shape
+    M = q0.shape[1]
+    dev, dt = k.device, k.dtype
+    for name, t, shp in (("q0", q0, (H, M, D)), ("q_fixed", q_fixed, (H, M, D)),
+                         ("k0", k0, (B, H, N, D)), ("k", k, (B, H, N, D)),
+                         ("v", v, (B, H, N, D)), ("y", y, (B, H, N, D))):
+        _check_tensor(name, t, shp, dt, dev)
+    _check_tensor("gate", gate, (H,), torch.float32, dev)
+    _call(lib.flarepp_mixer_fwd_noalloc, "flarepp_mixer_fwd_noalloc", B, H, N, M, D,
+          dtype_code(k), _ptr(q0), _ptr(q_fixed), _ptr(gate), _ptr(k0), _ptr(k), _ptr(v),
+          _ptr(y), _stream(stream))
     return y
 
 

@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "abi_common.hpp"
 #include "kernels.hpp"
@@ -179,12 +180,41 @@ hipError_t decode(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh
   return launch_decode(p.dtype, (int)p.D, d, s);
 }
 
+// Storage of the allocation-free forward: one array per device, owned by the
+// library for the life of the process.  Host code never uses the array's
+// name as an address: the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[FLAREPP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLAREPP_ERR_HIP;
+  if (dev >= kMaxDevices) return FLAREPP_ERR_UNSUPPORTED;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+        return FLAREPP_ERR_HIP;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return FLAREPP_OK;
+}
+
 // FLARE++ (v0 == k0, q_fixed and gate given) and simplified FLARE++ (own
 // synthesis values v0, q_fixed == gate == NULL: q is the synthesized query).
 int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, const void* q0,
                const void* q_fixed, const float* gate, const void* k0, const void* v0,
                const void* k, const void* v, void* y, void* ws, size_t ws_bytes, void* stream,
-               void* const* events, float* saved = nullptr, size_t saved_bytes = 0) {
+               void* const* events, float* saved = nullptr, size_t saved_bytes = 0,
+               bool scratch_ws = false) {
   const bool simplified = q_fixed == nullptr && gate == nullptr;
   if (!q0 || !k0 || !v0 || !k || !v || !y) return FLAREPP_ERR_INVALID_ARGUMENT;
   if (!aligned16(q0) || !aligned16(k0) || !aligned16(v0) || !aligned16(k) || !aligned16(v) ||
@@ -199,16 +229,25 @@ int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
       overlaps(y, tok, v, tok) || overlaps(y, tok, q0, lat) ||
       (!simplified && (overlaps(y, tok, q_fixed, lat) || overlaps(y, tok, gate, (size_t)H * 4))))
     return FLAREPP_ERR_INVALID_ARGUMENT;
-  if ((st = check_workspace(p, ws, ws_bytes)) != FLAREPP_OK) return st;
+  // scratch_ws: the library's own per-device array instead of a caller
+  // workspace (its size was checked by the caller; no caller buffer can
+  // overlap it); its address is taken after the device check
+  if (scratch_ws) {
+    if (p.total > ws_bytes) return FLAREPP_ERR_WORKSPACE;
+  } else if ((st = check_workspace(p, ws, ws_bytes)) != FLAREPP_OK) {
+    return st;
+  }
   Saved sv = saved_layout(B, H, N, M, D, saved);
   if (saved && (saved_bytes < sv.floats * sizeof(float) ||
                 (reinterpret_cast<uintptr_t>(saved) & 15)))
     return FLAREPP_ERR_WORKSPACE;
-  if (outputs_alias({{y, tok}, {saved, saved ? sv.floats * 4 : 0}, {ws, ws_bytes}},
+  if (outputs_alias({{y, tok}, {saved, saved ? sv.floats * 4 : 0},
+                     {ws, scratch_ws ? 0 : ws_bytes}},
                     {{q0, lat}, {q_fixed, lat}, {gate, gate ? (size_t)H * 4 : 0}, {k0, tok},
                      {v0, tok}, {k, tok}, {v, tok}}))
     return FLAREPP_ERR_INVALID_ARGUMENT;
   if ((st = check_device()) != FLAREPP_OK) return st;
+  if (scratch_ws && (st = scratch_for_current_device(&ws)) != FLAREPP_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float c = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
@@ -350,6 +389,19 @@ int simplified_flarepp_mixer_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int
   try {
     return mixer_impl(B, H, N, M, D, dtype, q0, nullptr, nullptr, k0, v0, k, v, y, workspace,
                       workspace_bytes, stream, nullptr);
+  } catch (...) {
+    return FLAREPP_ERR_HIP;
+  }
+}
+
+int flarepp_mixer_fwd_noalloc(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D,
+                              int dtype, const void* q0, const void* q_fixed, const float* gate,
+                              const void* k0, const void* k, const void* v, void* y,
+                              void* stream) {
+  try {
+    if (!q_fixed || !gate) return FLAREPP_ERR_INVALID_ARGUMENT;
+    return mixer_impl(B, H, N, M, D, dtype, q0, q_fixed, gate, k0, k0, k, v, y, nullptr,
+                      (size_t)FLAREPP_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, 0, true);
   } catch (...) {
     return FLAREPP_ERR_HIP;
   }

@@ -348,3 +348,29 @@ def test_probe_library_exports_its_header():
                                        ctypes.c_void_p]
     assert P.flarepp_probe_launch(0, 0, 1, None, None) == 1   # rejected before any launch
     assert P.flarepp_probe_launch(7, 1, 1, ctypes.c_void_p(0x1000), None) == 1
+
+
+def test_noalloc_validates_before_any_device_call():
+    """The allocation-free forward: shape errors and shapes whose workspace
+    exceeds the library's array are rejected before any HIP call."""
+    L = lib()
+    P = lambda n: FAKE[n]
+    args = [P(n) for n in ("q0", "qf", "gate", "k0", "k", "v", "y")]
+    import torch
+    if not torch.cuda.is_available():
+        assert L.flarepp_mixer_fwd_noalloc(1, 2, 1024, 16, 8, 1, *args, None) == HIP
+    assert L.flarepp_mixer_fwd_noalloc(1, 2, 0, 16, 8, 1, *args, None) == INV
+    assert L.flarepp_mixer_fwd_noalloc(1, 2, 1024, 16, 12, 1, *args, None) == UNS
+    big = (8, 16, 1 << 20, 512, 64)
+    assert L.flarepp_workspace_size(*big, 1) > fp.FLAREPP_NOALLOC_SCRATCH_BYTES
+    far = [ctypes.c_void_p((i + 1) << 40) for i in range(7)]   # 17 GB tensors, disjoint
+    assert L.flarepp_mixer_fwd_noalloc(*big, 1, *far, None) == WS
+    a = list(args)
+    a[1] = None                                     # q_fixed
+    assert L.flarepp_mixer_fwd_noalloc(1, 2, 1024, 16, 8, 1, *a, None) == INV
+    a = list(args)
+    a[6] = FAKE["k"]                                # y over k
+    assert L.flarepp_mixer_fwd_noalloc(1, 2, 1024, 16, 8, 1, *a, None) == INV
+    a = list(args)
+    a[4] = ctypes.c_void_p(FAKE["k"].value + 8)     # misaligned k
+    assert L.flarepp_mixer_fwd_noalloc(1, 2, 1024, 16, 8, 1, *a, None) == INV
