@@ -260,11 +260,13 @@ int flare_decode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
  * attention O = softmax_rows(s Q K^T) V with output gradient dO:
  *   dV = A^T dO,  dS = A * (dO V^T - rowsum(dO * O)),  dQ = s dS K,
  *   dK = s dS^T Q.
- * The backward supports bf16 and fp16 with D in {16, 32, 64} and M <= 512
- * (the token pass holds a head's latents in one workgroup's 160 KiB LDS; at
- * D = 64 with M > 384 it runs over two latent ranges, the second adding into
- * the gradients the first stored); other cases return
- * FLAREPP_ERR_UNSUPPORTED.  The token
+ * The backward supports every dtype with D in {8, 16, 32, 64} and M <= 512.
+ * bf16 and fp16 with D >= 16 run on the matrix cores (the token pass holds
+ * a head's latents in one workgroup's 160 KiB LDS; at D = 64 with M > 384 it
+ * runs over two latent ranges, the second adding into the gradients the
+ * first stored); fp32 inputs (every D) and D = 8 (below the matrix-core
+ * contraction length) run on VALU kernels in fp32 arithmetic, one thread per
+ * latent row or token.  Other cases return FLAREPP_ERR_UNSUPPORTED.  The token
  * tensors k, v, k0, y, dy and every gradient output (fp32) must be 16-byte
  * aligned, else FLAREPP_ERR_INVALID_ARGUMENT.  Gradient outputs must not
  * overlap any input or `saved`.  Results are deterministic (fixed reduction

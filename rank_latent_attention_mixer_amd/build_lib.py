@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "libflarepp.so")
 PROBE_LIB = os.path.join(PKG, "libflarepp_probe.so")
 PROBE_SOURCES = ["probe/peak_probe.hip"]
 
-SOURCES = ["encode_split.hip", "combine.hip", "decode.hip", "backward.hip", "flarepp_abi.cpp",
+SOURCES = ["encode_split.hip", "combine.hip", "decode.hip", "backward.hip", "backward_valu.hip",
+           "flarepp_abi.cpp",
            "backward_abi.cpp", "frontend.hip", "frontend_abi.cpp"]
 
 ARCH = "gfx950"

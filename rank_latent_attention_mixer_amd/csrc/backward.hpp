@@ -160,4 +160,73 @@ constexpr size_t kBwdTokMaxLds = 160 * 1024 - 512;
 // Launches over latent ranges the token pass takes for M latents (0: none fits).
 int bwd_tok_latent_ranges(int M, int D);
 
+// ---------------------------------------------------------------------------
+// VALU backward (backward_valu.hip): fp32 at every D, bf16 / fp16 at D = 8.
+// One thread per latent row (latent pass) or per token (token pass), fp32
+// arithmetic; weights A = 2^(S' - lse) from the saved normalisers, S' from
+// c q rounded to `round_dtype` as the forward's operand was.
+// ---------------------------------------------------------------------------
+struct BwdValuLatParams {
+  int mode;                     // kBwdLatDec / kBwdLatEnc / kBwdLatSyn
+  const void* qlat;             // latent rows (unscaled) [.., M, D] in qlat_dtype
+  int qlat_dtype;
+  int64_t q_b_stride, q_h_stride;
+  float c;                      // score factor s log2(e)
+  int round_dtype;              // dtype c q is rounded to (kF32: none)
+  const float* glat;            // fp32 [sets][M][D]: Dec z, Enc dz, Syn dqd
+  const float* lse_lat;         // Enc/Syn: [sets][M]
+  const float* negd_lat;        // Enc/Syn: -Delta per latent [sets][M]
+  const float* lse_tok;         // Dec: lse2 [sets][N]
+  const float* negd_tok;        // Dec: -Delta2 [sets][N]
+  const void* tk;               // token score rows [B,H,N,D] (k or k0)
+  const void* tg;               // token rows of G: Dec dy, Enc v, Syn values
+  float* part_y;                // [sets][nchunks][M][D]: s sum A G k
+  float* part_x;                // Dec: [sets][nchunks][M][D]: sum A dy
+  int B, H;
+  int64_t N;
+  int M;
+  int64_t chunk_tokens;
+  int nchunks;
+  float s;
+  const float* gate;            // Syn: heads with sigma == 0 write zeros
+};
+
+struct BwdValuTokParams {
+  int mode;                     // kBwdTokFlare / kBwdTokSyn
+  const void* qlat;
+  int qlat_dtype;
+  int64_t q_b_stride, q_h_stride;
+  float c;
+  int round_dtype;
+  const float* lat_z;           // Flare: z [sets][M][D]
+  const float* lat_g;           // Flare: dz; Syn: dqd [sets][M][D]
+  const float* lse_lat;         // Flare: lse1; Syn: lse0 [sets][M]
+  const float* negd_lat;        // Flare: -Delta1; Syn: -Delta0 [sets][M]
+  const float* lse_tok;         // Flare: lse2 [sets][N]
+  const float* negd_tok;        // Flare: -Delta2 [sets][N]
+  const void* tk;               // token score rows (k or k0)
+  const void* tdy;              // Flare: dy
+  const void* tw;               // Flare: v; Syn: the synthesis values (k0 or v0)
+  float* out_k;                 // dk (Syn: dk0, plus the value part when out_v is null)
+  float* out_v;                 // dv (Syn: dv0) or null
+  int B, H;
+  int64_t N;
+  int M;
+  float s_over_c;
+  const float* gate;
+};
+
+hipError_t launch_bwd_valu_lat(int dtype, int D, const BwdValuLatParams& p, hipStream_t s);
+hipError_t launch_bwd_valu_tok(int dtype, int D, const BwdValuTokParams& p, hipStream_t s);
+hipError_t launch_bwd_valu_negd(int dtype, int D, const void* dy, const void* y, float* out,
+                                int64_t rows, hipStream_t s);
+hipError_t launch_bwd_valu_sum(int D, const float* part, int nchunks, int M, int sets, float* dst,
+                               int accumulate, const float* w, float* negd, hipStream_t s);
+hipError_t launch_bwd_valu_batch_sum(const float* src, int B, int H, int M, int D, float* out,
+                                     const float* gate, float* dqd, hipStream_t s);
+hipError_t launch_bwd_valu_negd_rows(const float* a, const float* w, int64_t rows, int D,
+                                     float* out, hipStream_t s);
+hipError_t launch_bwd_valu_gate(const float* dq, const float* qd, int B, int H, int M, int D,
+                                const float* gate, float* dgate, hipStream_t s);
+
 }  // namespace flarepp

@@ -26,10 +26,57 @@ struct BwdPlan {
       off_cq0, off_dqdp, off_nd0, off_e0, off_dq0s, off_l2min, total;
 };
 
+// fp32 at every D, and D = 8 in any dtype, run on the VALU kernels
+// (backward_valu.hip); the rest on the matrix cores.
+bool bwd_on_valu(int dtype, int64_t D) { return dtype == FLAREPP_F32 || D < 16; }
+
+struct ValuPlan {
+  int64_t chunk_tokens;
+  int nchunks;
+  size_t off_nd2, off_py, off_px, off_dq, off_dz, off_nd1, off_dqd, off_nd0, off_dq0s, total;
+};
+
+int make_valu_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, ValuPlan* p) {
+  const int64_t BH = B * H;
+  // token chunks of the latent passes: about 2048 workgroups of 64 latents
+  const int64_t mblocks = (M + 63) / 64;
+  int64_t c = (2048 + BH * mblocks - 1) / (BH * mblocks);
+  const int64_t tiles = (N + 31) / 32;
+  if (c > tiles) c = tiles;
+  if (c < 1) c = 1;
+  p->chunk_tokens = (tiles + c - 1) / c * 32;
+  p->nchunks = (int)((N + p->chunk_tokens - 1) / p->chunk_tokens);
+  int64_t wgs;
+  if (!mul_ok(BH * mblocks, p->nchunks, &wgs) || wgs > 0x7FFFFFFF || BH > 65535)
+    return FLAREPP_ERR_INVALID_ARGUMENT;
+  const size_t f = 4, rows = (size_t)BH * M * D;
+  const size_t part = (size_t)BH * p->nchunks * M * D * f;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  p->off_nd2 = take((size_t)BH * N * f);
+  p->off_py = take(part);
+  p->off_px = take(part);
+  p->off_dq = take(rows * f);
+  p->off_dz = take(rows * f);
+  p->off_nd1 = take((size_t)BH * M * f);
+  p->off_dqd = take(rows * f);
+  p->off_nd0 = take((size_t)BH * M * f);
+  p->off_dq0s = take(rows * f);
+  p->total = off;
+  return FLAREPP_OK;
+}
+
 int make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, BwdPlan* p) {
   int st = check_shape(B, H, N, M, D, dtype);
   if (st != FLAREPP_OK) return st;
-  if (dtype == FLAREPP_F32 || D < 16) return FLAREPP_ERR_UNSUPPORTED;  // matrix-core path only
+  if (bwd_on_valu(dtype, D)) {
+    ValuPlan vp;
+    if ((st = make_valu_plan(B, H, N, M, D, &vp)) != FLAREPP_OK) return st;
+    std::memset(p, 0, sizeof(*p));
+    p->B = B; p->H = H; p->N = N; p->M = M; p->D = D; p->dtype = dtype;
+    p->total = vp.total;
+    return FLAREPP_OK;
+  }
   if (bwd_tok_latent_ranges((int)M, (int)D) < 1) return FLAREPP_ERR_UNSUPPORTED;
   p->B = B; p->H = H; p->N = N; p->M = M; p->D = D; p->dtype = dtype;
   p->Mpad = (int)((M + 31) / 32 * 32);
@@ -74,6 +121,95 @@ int make_bwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dty
   return FLAREPP_OK;
 }
 
+// The VALU sequence (fp32, or D = 8): the same passes as the matrix-core
+// sequence below, one thread per latent row or token.
+int bwd_valu_run(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, float scale,
+                 float c, bool pp, bool simplified, const void* q0, const float* gate,
+                 const void* k0, const void* v0, const void* q_flare, const void* k,
+                 const void* v, const void* y, const void* dy, const Saved& sv, float* dq0,
+                 float* dq_lat, float* dgate, float* dk0, float* dv0, float* dk, float* dv,
+                 void* ws, hipStream_t s) {
+  ValuPlan p;
+  int st = make_valu_plan(B, H, N, M, D, &p);
+  if (st != FLAREPP_OK) return st;
+  const int64_t BH = B * H;
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws_at(ws, off)); };
+  // -Delta2 = -(dy . y) per token
+  FLAREPP_TRY(launch_bwd_valu_negd(dtype, (int)D, dy, y, f32(p.off_nd2), BH * N, s));
+  // decoder over tokens: dq = s dS2^T k, dz = A2^T dy
+  BwdValuLatParams lp;
+  std::memset(&lp, 0, sizeof(lp));
+  lp.mode = kBwdLatDec;
+  if (pp) {
+    lp.qlat = sv.q; lp.qlat_dtype = FLAREPP_F32; lp.q_b_stride = H * M * D; lp.q_h_stride = M * D;
+  } else {
+    lp.qlat = q_flare; lp.qlat_dtype = dtype; lp.q_b_stride = 0; lp.q_h_stride = M * D;
+  }
+  lp.c = c; lp.round_dtype = dtype;
+  lp.glat = sv.z; lp.lse_tok = sv.lse2; lp.negd_tok = f32(p.off_nd2);
+  lp.tk = k; lp.tg = dy; lp.part_y = f32(p.off_py); lp.part_x = f32(p.off_px);
+  lp.B = (int)B; lp.H = (int)H; lp.N = N; lp.M = (int)M;
+  lp.chunk_tokens = p.chunk_tokens; lp.nchunks = p.nchunks; lp.s = scale;
+  FLAREPP_TRY(launch_bwd_valu_lat(dtype, (int)D, lp, s));
+  FLAREPP_TRY(launch_bwd_valu_sum((int)D, f32(p.off_py), p.nchunks, (int)M, (int)BH, f32(p.off_dq),
+                                  0, nullptr, nullptr, s));
+  // dz, and -Delta1 = -(dz . z) per latent
+  FLAREPP_TRY(launch_bwd_valu_sum((int)D, f32(p.off_px), p.nchunks, (int)M, (int)BH, f32(p.off_dz),
+                                  0, sv.z, f32(p.off_nd1), s));
+  // encoder over tokens: dq += s dS1 k
+  lp.mode = kBwdLatEnc;
+  lp.glat = f32(p.off_dz); lp.lse_lat = sv.lse1; lp.negd_lat = f32(p.off_nd1);
+  lp.lse_tok = nullptr; lp.negd_tok = nullptr; lp.tg = v; lp.part_x = nullptr;
+  FLAREPP_TRY(launch_bwd_valu_lat(dtype, (int)D, lp, s));
+  FLAREPP_TRY(launch_bwd_valu_sum((int)D, f32(p.off_py), p.nchunks, (int)M, (int)BH, f32(p.off_dq),
+                                  1, nullptr, nullptr, s));
+  // per token, both attentions: dk = s (dS2 + dS1^T) q, dv = A1^T dz
+  BwdValuTokParams kp;
+  std::memset(&kp, 0, sizeof(kp));
+  kp.mode = kBwdTokFlare;
+  kp.qlat = lp.qlat; kp.qlat_dtype = lp.qlat_dtype;
+  kp.q_b_stride = lp.q_b_stride; kp.q_h_stride = lp.q_h_stride;
+  kp.c = c; kp.round_dtype = dtype;
+  kp.lat_z = sv.z; kp.lat_g = f32(p.off_dz); kp.lse_lat = sv.lse1; kp.negd_lat = f32(p.off_nd1);
+  kp.lse_tok = sv.lse2; kp.negd_tok = f32(p.off_nd2);
+  kp.tk = k; kp.tdy = dy; kp.tw = v; kp.out_k = dk; kp.out_v = dv;
+  kp.B = (int)B; kp.H = (int)H; kp.N = N; kp.M = (int)M; kp.s_over_c = scale / c;
+  FLAREPP_TRY(launch_bwd_valu_tok(dtype, (int)D, kp, s));
+  if (!pp) {  // FLARE: the latents are shared by the batch
+    FLAREPP_TRY(launch_bwd_valu_batch_sum(f32(p.off_dq), (int)B, (int)H, (int)M, (int)D, dq_lat,
+                                          nullptr, nullptr, s));
+    return FLAREPP_OK;
+  }
+  // FLARE++: dq_fixed = sum_b dq, dqd = sigma dq, dgate; simplified: dqd = dq
+  FLAREPP_TRY(launch_bwd_valu_batch_sum(f32(p.off_dq), (int)B, (int)H, (int)M, (int)D,
+                                        simplified ? nullptr : dq_lat,
+                                        simplified ? nullptr : gate, f32(p.off_dqd), s));
+  if (!simplified)
+    FLAREPP_TRY(launch_bwd_valu_gate(f32(p.off_dq), sv.qd, (int)B, (int)H, (int)M, (int)D, gate,
+                                     dgate, s));
+  // -Delta0 = -(dqd . q_dyn) per latent
+  FLAREPP_TRY(launch_bwd_valu_negd_rows(f32(p.off_dqd), sv.qd, BH * M, (int)D, f32(p.off_nd0), s));
+  // synthesis over tokens: dq0 = s dS0 k0 per (b, h), then summed over the batch
+  lp.mode = kBwdLatSyn;
+  lp.qlat = q0; lp.qlat_dtype = dtype; lp.q_b_stride = 0; lp.q_h_stride = M * D;
+  lp.glat = f32(p.off_dqd); lp.lse_lat = sv.lse0; lp.negd_lat = f32(p.off_nd0);
+  lp.tk = k0; lp.tg = v0; lp.gate = gate;
+  FLAREPP_TRY(launch_bwd_valu_lat(dtype, (int)D, lp, s));
+  FLAREPP_TRY(launch_bwd_valu_sum((int)D, f32(p.off_py), p.nchunks, (int)M, (int)BH,
+                                  f32(p.off_dq0s), 0, nullptr, nullptr, s));
+  FLAREPP_TRY(launch_bwd_valu_batch_sum(f32(p.off_dq0s), (int)B, (int)H, (int)M, (int)D, dq0,
+                                        nullptr, nullptr, s));
+  // dk0 = s dS0^T q0 (+ A0^T dqd when k0 is also the value), dv0 = A0^T dqd
+  kp.mode = kBwdTokSyn;
+  kp.qlat = q0; kp.qlat_dtype = dtype; kp.q_b_stride = 0; kp.q_h_stride = M * D;
+  kp.lat_z = nullptr; kp.lat_g = f32(p.off_dqd); kp.lse_lat = sv.lse0;
+  kp.negd_lat = f32(p.off_nd0); kp.lse_tok = nullptr; kp.negd_tok = nullptr;
+  kp.tk = k0; kp.tdy = nullptr; kp.tw = v0;
+  kp.out_k = dk0; kp.out_v = simplified ? dv0 : nullptr; kp.gate = gate;
+  FLAREPP_TRY(launch_bwd_valu_tok(dtype, (int)D, kp, s));
+  return FLAREPP_OK;
+}
+
 // Shared by FLARE++ (q0 non-null, v0 == k0: synthesis and gate), the
 // simplified mixer (q0 non-null, v0 its own tensor, no gate: q = q_dyn) and
 // FLARE (q0 null, q given, caller scale).
@@ -104,7 +240,8 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   for (const void* in : {k, v, y, dy, pp ? k0 : nullptr, pp ? v0 : nullptr})
     if (in && !aligned16(in)) return FLAREPP_ERR_INVALID_ARGUMENT;
   const size_t tokf = (size_t)(B * H * N * D) * 4, latf = (size_t)(H * M * D) * 4;
-  const size_t toke = (size_t)(B * H * N * D) * 2, late = (size_t)(H * M * D) * 2;
+  const size_t es = (size_t)esize_of(dtype);
+  const size_t toke = (size_t)(B * H * N * D) * es, late = (size_t)(H * M * D) * es;
   if (ws == nullptr || ws_bytes < p.total || ((uintptr_t)ws % kAlign) != 0)
     return FLAREPP_ERR_WORKSPACE;
   // the workspace is written by the kernels, so it counts as an output
@@ -121,6 +258,9 @@ int bwd_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype, f
   // the forward's score factor, bit for bit (it rounds c q to the operand type)
   const float c = pp ? (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634)
                      : (float)((double)scale * 1.4426950408889634);
+  if (bwd_on_valu(dtype, D))
+    return bwd_valu_run(B, H, N, M, D, dtype, scale, c, pp, simplified, q0, gate, k0, v0, q_flare,
+                        k, v, y, dy, sv, dq0, dq_lat, dgate, dk0, dv0, dk, dv, ws, s);
   // weights normalised over the N tokens are taken times 2^shift so that
   // ~1/N stays a normal fp16 number while P times a gradient term stays
   // far below the fp16 maximum

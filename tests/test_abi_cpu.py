@@ -203,8 +203,9 @@ def test_saved_size_formula():
     ((1, 1, 100, 416, 64, 1), True),
     ((1, 1, 100, 512, 64, 2), True),     # token pass over two latent ranges
     ((1, 1, 100, 513, 64, 1), False),    # M above the library's maximum
-    ((1, 1, 100, 64, 8, 1), False),      # D = 8: no matrix-core backward
-    ((1, 1, 100, 64, 32, 0), False),     # fp32
+    ((1, 1, 100, 64, 8, 1), True),       # D = 8: the VALU backward
+    ((1, 1, 100, 64, 32, 0), True),      # fp32: the VALU backward
+    ((1, 1, 100, 64, 12, 0), False),     # D outside {8, 16, 32, 64}
     ((1, 1, 0, 64, 32, 1), False),
 ])
 def test_bwd_workspace_size(args, ok):
@@ -234,7 +235,7 @@ def _bwd(B=1, H=2, N=1024, M=16, D=32, dt=1, saved_bytes=None, wsb=None, **kw):
     (dict(q0=None), INV), (dict(gate=None), INV), (dict(k0=None), INV), (dict(k=None), INV),
     (dict(y=None), INV), (dict(dy=None), INV), (dict(saved=None), INV), (dict(dq0=None), INV),
     (dict(dqf=None), INV), (dict(dgate=None), INV), (dict(dk0=None), INV), (dict(dk=None), INV),
-    (dict(dv=None), INV), (dict(D=8), UNS), (dict(dt=0), UNS), (dict(M=513), UNS),
+    (dict(dv=None), INV), (dict(D=12), UNS), (dict(dt=5), INV), (dict(M=513), UNS),
     (dict(saved_bytes=64), WS), (dict(ws=None), WS), (dict(wsb=1), WS),
     (dict(dk="k"), INV), (dict(dv="dy"), INV), (dict(dk0="saved"), INV),
     (dict(dy=ctypes.c_void_p(0x10000000 * 27 + 8)), INV),       # misaligned dy
@@ -374,3 +375,17 @@ def test_noalloc_validates_before_any_device_call():
     a = list(args)
     a[4] = ctypes.c_void_p(FAKE["k"].value + 8)     # misaligned k
     assert L.flarepp_mixer_fwd_noalloc(1, 2, 1024, 16, 8, 1, *a, None) == INV
+
+
+def test_bwd_fp32_and_d8_are_supported():
+    """fp32 (every D) and D = 8 (every dtype) run on the VALU backward: a
+    workspace size is reported and a valid call only fails for want of a
+    device."""
+    L = fp.load_library()
+    for dt in (0, 1, 2):
+        for D in (8, 16, 32, 64):
+            assert L.flarepp_bwd_workspace_size(2, 3, 1000, 40, D, dt) > 0, (dt, D)
+    import torch
+    if not torch.cuda.is_available():
+        assert _bwd(dt=0) == HIP
+        assert _bwd(D=8) == HIP

@@ -4,7 +4,9 @@ the fp64 oracle gradients (oracle.flarepp_bwd_ref / oracle.flare_bwd_ref).
 Inputs and the output gradient dy are seeded and rounded to the operand
 type; the oracle takes those exact values in fp64.  Bar, per gradient
 tensor: max|g - g_ref| / max|g_ref| <= 2e-2 for bf16/fp16 operands (fp32
-accumulation, fp32 gradients out), the bar of the forward pass.
+accumulation, fp32 gradients out) and <= 1e-5 for fp32 inputs, the bars of
+the forward pass.  fp32 inputs (every D) and D = 8 (every dtype) run the
+VALU backward; the rest the matrix-core passes.
 """
 
 from __future__ import annotations
@@ -20,8 +22,8 @@ from flarepp_workloads import WORKLOADS, make_cotangent, make_inputs, make_rando
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "fp16": 2e-2}
-TDT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+TOL = {"bf16": 2e-2, "fp16": 2e-2, "fp32": 1e-5}
+TDT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 NAMES = ("q0", "q_fixed", "gate", "k0", "k", "v")
 TOKEN_GRADS = ("dk0", "dk", "dv")
 LATENT_GRADS = ("dq0", "dq_fixed")
@@ -345,3 +347,78 @@ def test_simplified_bwd_vs_oracle(fp, B, H, N, M, D, dtype):
     note("[bwd] simplified " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
         assert e <= TOL[dtype], (n, e)
+
+
+# ---------------------------------------------------------------- VALU backward
+VALU_SHAPES = [
+    # (B, H, N, M, D, dtype, gate logits)
+    (2, 3, 700, 80, 32, "fp32", [0.3, -np.inf, 1.2]),     # ragged; one closed head
+    (1, 2, 300, 33, 64, "fp32", [1.0, -1.0]),
+    (1, 2, 1000, 64, 16, "fp32", [-0.5, 2.0]),
+    (2, 2, 513, 100, 8, "fp32", [0.0, np.inf]),           # gate fully open on one head
+    (1, 2, 1024, 16, 8, "fp32", [0.7, -0.2]),             # the tiny fp32 workload's shape
+    (1, 1, 37, 1, 8, "fp32", [0.5]),                      # a single latent
+    (1, 2, 129, 512, 16, "fp32", [0.2, -0.7]),            # maximum M
+    (2, 3, 700, 80, 8, "bf16", [0.3, -np.inf, 1.2]),      # D = 8 below the matrix-core K
+    (1, 2, 1000, 64, 8, "fp16", [-0.5, 2.0]),
+    (1, 2, 129, 512, 8, "bf16", [0.2, -0.7]),
+    (4, 32, 9, 24, 8, "fp16", list(np.linspace(-2.0, 2.0, 32))),  # 128 heads
+]
+
+
+@pytest.mark.parametrize("B,H,N,M,D,dtype,gate", VALU_SHAPES)
+def test_valu_flarepp_bwd_vs_oracle(fp, B, H, N, M, D, dtype, gate):
+    note(f"[bwd] valu flarepp B={B} H={H} N={N} M={M} D={D} {dtype}")
+    x = make_random_inputs(B, H, N, M, D, dtype, seed=131 + N, gate=np.array(gate, np.float32))
+    dy = make_cotangent(B, H, N, D, dtype, seed=177 + N)
+    got, _ = run_flarepp_bwd(fp, x, dy, dtype)
+    for n, g in got.items():
+        assert np.all(np.isfinite(g)), n
+    ref = oracle.flarepp_bwd_ref(**f64(x), dy=np.asarray(dy, np.float64))
+    check_flarepp(f"valu B={B} H={H} N={N} M={M} D={D} {dtype}", got, ref, dtype)
+    for h in np.nonzero(np.isneginf(np.asarray(gate)))[0]:
+        assert np.all(got["dq0"][h] == 0) and np.all(got["dk0"][:, h] == 0)
+        assert got["dgate"][h] == 0
+
+
+@pytest.mark.parametrize("B,H,N,M,D,dtype,scale", [
+    (2, 2, 900, 96, 32, "fp32", 0.2),
+    (1, 3, 500, 40, 8, "fp32", 1.0),                      # the FLARE listing's scale
+    (1, 1, 700, 256, 64, "fp32", 0.125),
+    (1, 2, 7, 20, 8, "bf16", 0.5),
+    (2, 2, 600, 48, 8, "fp16", 1.0 / np.sqrt(8.0)),
+])
+def test_valu_flare_bwd_vs_oracle(fp, B, H, N, M, D, dtype, scale):
+    note(f"[bwd] valu flare B={B} H={H} N={N} M={M} D={D} {dtype} scale={scale}")
+    x = make_random_inputs(B, H, N, M, D, dtype, seed=15 + N)
+    dy = make_cotangent(B, H, N, D, dtype, seed=16 + N)
+    q, k, v = dev(x["q_fixed"], dtype), dev(x["k"], dtype), dev(x["v"], dtype)
+    y, saved = fp.flare_mixer_fwd_train(q, k, v, scale)
+    g = fp.flare_mixer_bwd(q, k, v, scale, y, dev(dy, dtype), saved)
+    torch.cuda.synchronize()
+    ref = oracle.flare_bwd_ref(np.asarray(x["q_fixed"], np.float64),
+                               np.asarray(x["k"], np.float64), np.asarray(x["v"], np.float64),
+                               scale, np.asarray(dy, np.float64))
+    errs = {n: rel_err(g[n].cpu().numpy(), r) for n, r in zip(("dq", "dk", "dv"), ref)}
+    note("[bwd] valu flare " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[dtype], (n, e)
+
+
+@pytest.mark.parametrize("B,H,N,M,D,dtype", [
+    (2, 2, 700, 64, 32, "fp32"),
+    (1, 2, 400, 40, 8, "fp32"),
+    (1, 2, 500, 32, 8, "bf16"),
+])
+def test_valu_simplified_bwd_vs_oracle(fp, B, H, N, M, D, dtype):
+    test_simplified_bwd_vs_oracle(fp, B, H, N, M, D, dtype)
+
+
+def test_valu_bwd_deterministic(fp):
+    B, H, N, M, D, dtype = 2, 2, 900, 72, 32, "fp32"
+    x = make_random_inputs(B, H, N, M, D, dtype, seed=8, gate=np.array([0.4, -0.9], np.float32))
+    dy = make_cotangent(B, H, N, D, dtype, seed=9)
+    a, _ = run_flarepp_bwd(fp, x, dy, dtype)
+    b, _ = run_flarepp_bwd(fp, x, dy, dtype)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
