@@ -293,6 +293,25 @@ def probe_peaks():
         t = start.elapsed_time(stop) / 10 / 1e3
         res[name] = lib.flarepp_probe_work(which, blocks, iters) / t
         log(f"[probe] {name}: {t * 1e3:.3f} ms per launch")
+    # sustained (about a second each): the same products on random-bit and
+    # on all-ones operands; the ratio is the clock the power limit takes away
+    # when operand bits toggle
+    for which, name in ((2, "mfma_bf16_random_sustained"), (3, "mfma_bf16_ones_sustained")):
+        launches, t_total = 0, 0.0
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        while t_total < 1.0:
+            start.record()
+            for _ in range(20):
+                lib.flarepp_probe_launch(which, blocks, iters, ctypes.c_void_p(out.data_ptr()), stream)
+            stop.record()
+            torch.cuda.synchronize()
+            t_total += start.elapsed_time(stop) / 1e3
+            launches += 20
+        # the rate of the last 20 launches, after the clock has settled
+        t = start.elapsed_time(stop) / 20 / 1e3
+        res[name] = lib.flarepp_probe_work(which, blocks, iters) / t
+        log(f"[probe] {name}: {t * 1e3:.3f} ms per launch after {t_total:.2f} s")
     from flarepp_workloads import WORKLOADS
     w = WORKLOADS["million_token_bf16"]
     exps = 3 * w.B * w.H * w.N * w.M  # one forward, every gate open
@@ -302,6 +321,8 @@ def probe_peaks():
         "mfma_bf16_tflops_published": PEAK_BF16_TFLOPS,
         "exp_f32_per_s_measured": float(f"{res['exp_f32']:.4g}"),
         "exp_ms_per_million_token_forward": float(f"{exps / res['exp_f32'] * 1e3:.4g}"),
+        "mfma_bf16_tflops_sustained_random_operands": round(res["mfma_bf16_random_sustained"] / 1e12, 1),
+        "mfma_bf16_tflops_sustained_ones_operands": round(res["mfma_bf16_ones_sustained"] / 1e12, 1),
     }), flush=True)
     return 0
 

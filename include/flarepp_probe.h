@@ -11,7 +11,18 @@
 extern "C" {
 #endif
 
-enum { FLAREPP_PROBE_MFMA_BF16 = 0, FLAREPP_PROBE_EXP_F32 = 1 };
+/* MFMA_BF16: eight accumulator chains, near-constant operands;
+ * EXP_F32: eight exponential chains per lane;
+ * MFMA_BF16_RANDOM / MFMA_BF16_ONES: the same products with operands of
+ * random sign and mantissa, or all 1.0 -- run for a second or more, the
+ * pair shows how far the power limit lowers the clock when operand bits
+ * toggle as real data does. */
+enum {
+  FLAREPP_PROBE_MFMA_BF16 = 0,
+  FLAREPP_PROBE_EXP_F32 = 1,
+  FLAREPP_PROBE_MFMA_BF16_RANDOM = 2,
+  FLAREPP_PROBE_MFMA_BF16_ONES = 3
+};
 
 /* Launches probe `which` with `blocks` workgroups of 256 threads, each lane
  * running `iters` iterations; writes one float per thread to `out` (device,

@@ -48,6 +48,51 @@ __global__ __launch_bounds__(256) void exp_probe(float* out, int iters, float se
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// The matrix cores' sustained rate depends on the data they multiply: the
+// chip's power limit lowers the clock further when the operand bits toggle.
+// Both variants issue the same products (four independent accumulators,
+// operands rotating through eight registers); RANDOM fills the operands with
+// hashed bf16 values of random sign and mantissa in [1, 2) (the toggling of
+// real activations), the other with 1.0 everywhere.
+__device__ __forceinline__ unsigned probe_hash(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+template <bool RANDOM>
+__global__ __launch_bounds__(256) void mfma_data_probe(float* out, int iters) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  bf16x8 r[8];
+  for (int j = 0; j < 8; ++j) {
+    u32x4 t;
+    for (int e = 0; e < 4; ++e) {
+      const unsigned h = probe_hash((blockIdx.x * 256u + threadIdx.x) * 37u + j * 5u + e);
+      const unsigned lo = 0x3F80u | (h & 0x807Fu), hi = 0x3F80u | ((h >> 16) & 0x807Fu);
+      t[e] = RANDOM ? (lo | (hi << 16)) : 0x3F803F80u;
+    }
+    r[j] = __builtin_bit_cast(bf16x8, t);
+  }
+  f32x16 c[4];
+  for (int j = 0; j < 4; ++j)
+    for (int v = 0; v < 16; ++v) c[j][v] = 0.f;
+  for (int it = 0; it < iters; it += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[(u + j) & 7], r[(u + 2 * j + 1) & 7], c[j],
+                                                        0, 0, 0);
+  }
+  float s = 0.f;
+  for (int j = 0; j < 4; ++j)
+    for (int v = 0; v < 16; ++v) s += c[j][v];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -59,6 +104,10 @@ int flarepp_probe_launch(int which, int blocks, int iters, float* out, void* str
     hipLaunchKernelGGL(mfma_probe, dim3(blocks), dim3(256), 0, s, out, iters, 1e-3f);
   else if (which == FLAREPP_PROBE_EXP_F32)
     hipLaunchKernelGGL(exp_probe, dim3(blocks), dim3(256), 0, s, out, iters, 1e-3f);
+  else if (which == FLAREPP_PROBE_MFMA_BF16_RANDOM)
+    hipLaunchKernelGGL(mfma_data_probe<true>, dim3(blocks), dim3(256), 0, s, out, iters);
+  else if (which == FLAREPP_PROBE_MFMA_BF16_ONES)
+    hipLaunchKernelGGL(mfma_data_probe<false>, dim3(blocks), dim3(256), 0, s, out, iters);
   else
     return 1;
   return hipGetLastError() == hipSuccess ? 0 : 4;
@@ -69,6 +118,8 @@ double flarepp_probe_work(int which, int blocks, int iters) {
   if (which == FLAREPP_PROBE_MFMA_BF16)  // per wave: iters x 8 products of 2*32*32*16 flops
     return (lanes / 64.0) * iters * 8.0 * 2.0 * 32 * 32 * 16;
   if (which == FLAREPP_PROBE_EXP_F32) return lanes * iters * 8.0;  // exponentials
+  if (which == FLAREPP_PROBE_MFMA_BF16_RANDOM || which == FLAREPP_PROBE_MFMA_BF16_ONES)
+    return (lanes / 64.0) * ((iters + 7) / 8 * 8) * 4.0 * 2.0 * 32 * 32 * 16;
   return 0.0;
 }
 
