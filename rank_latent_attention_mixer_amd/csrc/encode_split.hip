@@ -29,8 +29,15 @@ constexpr int kMaxWaves = 16 / kNC;   // waves per workgroup for M = 512
 #ifndef FLAREPP_ENC_TILE
 #define FLAREPP_ENC_TILE 128
 #endif
-constexpr int kTJ = FLAREPP_ENC_TILE;  // tokens per LDS tile
-constexpr int kGPT = kTJ / 32;         // 32-key groups per tile
+constexpr int kTJ = FLAREPP_ENC_TILE;  // tokens per LDS tile (chunk granularity)
+// Tiles of 64 tokens at D = 64: with 128 the unrolled tile body held 268
+// VGPRs and two staged tensors took 96 KB of LDS -- one 4-wave workgroup,
+// one wave per SIMD; with 64 it fits 204 VGPRs and 48 KB, two waves per
+// SIMD (measured -20% for the encoder at B8 H16 N16384 M128 D64 fp16).
+template <int D>
+constexpr int kTileTokens = D >= 64 ? 64 : kTJ;
+template <int D>
+constexpr int kMinWaves = D >= 64 ? 2 : 1;  // waves per SIMD the registers must allow
 // LDS tiles rotate over three buffers: with the score product running one
 // group ahead, a wave may still read tile t-1 while others fill tile t+1.
 constexpr int kNBUF = 3;
@@ -44,7 +51,7 @@ struct TileLayout {
   static constexpr int ROWB = 2 * D;           // bytes per token row
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int RPB = 256 / ROWB;       // rows per 256 bytes (all banks)
-  static constexpr int TILEB = kTJ * ROWB;     // bytes per tile per tensor
+  static constexpr int TILEB = kTileTokens<D> * ROWB;  // bytes per tile per tensor
   __device__ __forceinline__ static int swz(int row) { return (row / RPB) % CPR; }
   __device__ __forceinline__ static int offset(int row, int byte) {  // byte within row
     return row * ROWB + (((byte >> 4) ^ swz(row)) << 4) + (byte & 15);
@@ -52,7 +59,9 @@ struct TileLayout {
 };
 
 template <typename T, int D, int NW, bool SHARED_KV>
-__global__ __launch_bounds__(64 * NW) void encode_split_kernel(EncodeParams a) {
+__global__ __launch_bounds__(64 * NW, kMinWaves<D>) void encode_split_kernel(EncodeParams a) {
+  constexpr int kTJ = kTileTokens<D>;  // tokens per LDS tile
+  constexpr int kGPT = kTJ / 32;       // 32-key groups per tile
   using Tile = FlashTile<T, D, kNC>;
   using V8 = typename Tile::V8;
   using L = TileLayout<D>;
