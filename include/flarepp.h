@@ -152,7 +152,8 @@ int flarepp_mixer_fwd_noalloc(int64_t B, int64_t H, int64_t N, int64_t M, int64_
  * Same computation as flarepp_mixer_fwd, with timing marks for profiling.
  * `events` points to FLAREPP_TIMED_EVENTS hipEvent_t handles created by the
  * caller; the call records them on `stream` around its launches:
- *   events[0] start                      events[1] after the seed operand copy
+ *   events[0] start                      events[1] = events[0] (no launch: the
+ *                                         synthesis encoder scales the seeds itself)
  *   events[2] after the synthesis encoder events[3] after the gated combine
  *   events[4] after the encoder          events[5] after the value combine
  *   events[6] after the decoder

@@ -87,9 +87,14 @@ decode_kernel(DecodeParams a) {
   {
     const T* qg = reinterpret_cast<const T*>(a.q) + b * a.q_b_stride + hd * a.q_h_stride;
     constexpr int G8 = D / 8;
+    const bool raw = a.qscale > 0.f;  // caller latents [.., M, D]: scale, zero rows >= M
     for (int u = tid; u < Mk * G8; u += 64 * kNW) {
       const int row = u / G8, e = u - row * G8;
-      *reinterpret_cast<u32x4*>(&qs[row * KP + 8 * e]) = ldg16(qg + (int64_t)row * D + 8 * e);
+      u32x4 w;
+      if (!raw) w = ldg16(qg + (int64_t)row * D + 8 * e);
+      else if (row < a.M) w = scaled8<T>(qg + (int64_t)row * D + 8 * e, a.qscale);
+      else w = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&qs[row * KP + 8 * e]) = w;
     }
     const T* zg = reinterpret_cast<const T*>(a.zt) + (int64_t)bh * DV * a.Mpad;
     const int zg8 = Mk / 8;
@@ -389,7 +394,8 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams a) {
     const int tv = min(TM, a.M - mb);
     for (int e = tid; e < TM * D; e += blockDim.x) {
       const int j = e / D, d = e - j * D;
-      qsm[j][d] = j < tv ? qb[(int64_t)(mb + j) * D + d] : 0.f;
+      const float qv = j < tv ? qb[(int64_t)(mb + j) * D + d] : 0.f;
+      qsm[j][d] = a.qscale > 0.f ? a.qscale * qv : qv;
       zsm[j][d] = j < tv ? zb[(int64_t)(mb + j) * D + d] : 0.f;
     }
     __syncthreads();

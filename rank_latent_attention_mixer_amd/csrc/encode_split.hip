@@ -105,13 +105,18 @@ __global__ __launch_bounds__(64 * NW, kMinWaves<D>) void encode_split_kernel(Enc
   {
     const T* qb = reinterpret_cast<const T*>(a.q) + b * a.q_b_stride + hd * a.q_h_stride;
     const int col = wave * 32 * kNC + r;
+    const bool raw = a.qscale > 0.f;  // caller latents [.., M, D]: scale, zero rows >= M
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
 #pragma unroll
       for (int kd = 0; kd < KD; ++kd) {
-        const int d0 = 16 * kd + 8 * h;
-        if (d0 < D) st.q[cb][kd] = bitcast_u4<V8>(ldg16(qb + (int64_t)(col + 32 * cb) * D + d0));
-        else st.q[cb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+        const int d0 = 16 * kd + 8 * h, row = col + 32 * cb;
+        if (d0 >= D || (raw && row >= a.M))
+          st.q[cb][kd] = bitcast_u4<V8>(u32x4{0u, 0u, 0u, 0u});
+        else if (raw)
+          st.q[cb][kd] = bitcast_u4<V8>(scaled8<T>(qb + (int64_t)row * D + d0, a.qscale));
+        else
+          st.q[cb][kd] = bitcast_u4<V8>(ldg16(qb + (int64_t)row * D + d0));
       }
     }
   }
@@ -402,7 +407,8 @@ __global__ __launch_bounds__(512) void encode_split_f32_kernel(EncodeParams a) {
   float q[D], o[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    q[d] = qb[(int64_t)m * D + d];
+    if (a.qscale > 0.f) q[d] = m < a.M ? a.qscale * qb[(int64_t)m * D + d] : 0.f;
+    else q[d] = qb[(int64_t)m * D + d];
     o[d] = 0.f;
   }
   float mref = -__builtin_inff(), l = 0.f;

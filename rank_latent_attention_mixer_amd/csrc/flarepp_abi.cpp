@@ -49,7 +49,7 @@ struct Plan {
   int64_t chunk_tokens;
   int nchunks;
   int dec_wg_per_bh;
-  size_t off_pm, off_pl, off_po, off_q0, off_q, off_z, off_redo, total;
+  size_t off_pm, off_pl, off_po, off_q, off_z, off_redo, total;
 };
 
 int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
@@ -89,7 +89,6 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   p->off_pm = off; off = align_up(off + stat);
   p->off_pl = off; off = align_up(off + stat);
   p->off_po = off; off = align_up(off + stat * D);
-  p->off_q0 = off; off = align_up(off + (size_t)H * p->Mpad * D * es);
   p->off_q = off;  off = align_up(off + (size_t)BH * p->Mpad * D * es);
   p->off_z = off;
   off = align_up(off + (dtype == FLAREPP_F32 ? (size_t)BH * p->Mpad * D * 4
@@ -107,10 +106,13 @@ int check_workspace(const Plan& p, void* ws, size_t bytes) {
   return FLAREPP_OK;
 }
 
+// qscale > 0: q is the caller's latents [.., M, D]; the kernel forms the
+// operand (dtype)(qscale q) as it loads them.  0: q is an operand the
+// combine kernel wrote ([.., Mpad, D], prescaled).
 EncodeParams encode_params(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh,
-                           const void* k, const void* v, const float* gate) {
+                           const void* k, const void* v, const float* gate, float qscale = 0.f) {
   EncodeParams e;
-  e.q = q; e.q_b_stride = qb; e.q_h_stride = qh;
+  e.q = q; e.q_b_stride = qb; e.q_h_stride = qh; e.qscale = qscale;
   e.k = k; e.v = v;
   e.B = (int)p.B; e.H = (int)p.H; e.N = p.N; e.M = (int)p.M; e.Mpad = p.Mpad;
   e.chunk_tokens = p.chunk_tokens; e.nchunks = p.nchunks;
@@ -136,23 +138,6 @@ CombineParams combine_base(const Plan& p, void* ws) {
   return c;
 }
 
-// Operand copy of caller latents: out = scale*log2(e) * in, [sets][Mpad][D].
-hipError_t prep_latents(const Plan& p, void* ws, size_t off, const void* in, int64_t in_b_stride,
-                        int nsets, float cscale, hipStream_t s) {
-  CombineParams c = combine_base(p, ws);
-  c.nsets = nsets;
-  c.nchunks = 0;
-  c.mode = kModeQuery;
-  c.fixed = in;
-  c.fixed_b_stride = in_b_stride;
-  c.fixed_dtype = p.dtype;
-  c.force_fixed = 1;
-  c.cscale = cscale;
-  c.out = ws_at(ws, off);
-  c.out_kind = p.dtype == FLAREPP_F32 ? kOutNatural32 : kOutNatural;
-  return launch_combine(c, s);
-}
-
 hipError_t value_operand(const Plan& p, void* ws, int nchunks, const float* z_in, float* z_out,
                          hipStream_t s, float* lse_out = nullptr) {
   CombineParams c = combine_base(p, ws);
@@ -168,10 +153,10 @@ hipError_t value_operand(const Plan& p, void* ws, int nchunks, const float* z_in
 }
 
 hipError_t decode(const Plan& p, void* ws, const void* q, int64_t qb, int64_t qh, const void* k,
-                  void* y, hipStream_t s, float* lse_out = nullptr) {
+                  void* y, hipStream_t s, float* lse_out = nullptr, float qscale = 0.f) {
   DecodeParams d;
   d.lse_out = lse_out;
-  d.q = q; d.q_b_stride = qb; d.q_h_stride = qh;
+  d.q = q; d.q_b_stride = qb; d.q_h_stride = qh; d.qscale = qscale;
   d.zt = ws_at(ws, p.off_z);
   d.redo = reinterpret_cast<unsigned long long*>(ws_at(ws, p.off_redo));
   d.k = k; d.y = y;
@@ -257,11 +242,11 @@ int mixer_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
   };
   FLAREPP_TRY(mark(0));
-  // 1. seeds as operand, 2. synthesis partials (closed-gate heads skipped)
-  FLAREPP_TRY(prep_latents(p, ws, p.off_q0, q0, 0, (int)H, c, s));
+  // 1. synthesis partials (closed-gate heads skipped); the seeds are scaled
+  // as the encoder loads them, so nothing runs between marks 0 and 1
   FLAREPP_TRY(mark(1));
   FLAREPP_TRY(launch_encode(dtype, (int)D,
-                            encode_params(p, ws, ws_at(ws, p.off_q0), 0, qh, k0, v0, gate), s));
+                            encode_params(p, ws, q0, 0, M * D, k0, v0, gate, c), s));
   FLAREPP_TRY(mark(2));
   // 3. q = q_fixed + sigma * q_dyn (simplified: q = q_dyn), per (b, h), as operand
   {
@@ -323,13 +308,12 @@ int flare_impl(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float c = (float)((double)scale * 1.4426950408889634);
-  const int64_t qh = (int64_t)p.Mpad * D;
-  FLAREPP_TRY(prep_latents(p, ws, p.off_q0, q, 0, (int)H, c, s));
+  // the latents are scaled as the encoder and the decoder load them
   FLAREPP_TRY(launch_encode(dtype, (int)D,
-                            encode_params(p, ws, ws_at(ws, p.off_q0), 0, qh, k, v, nullptr), s));
+                            encode_params(p, ws, q, 0, M * D, k, v, nullptr, c), s));
   FLAREPP_TRY(value_operand(p, ws, p.nchunks, nullptr, saved ? sv.z : nullptr, s,
                             saved ? sv.lse1 : nullptr));
-  FLAREPP_TRY(decode(p, ws, ws_at(ws, p.off_q0), 0, qh, k, y, s, saved ? sv.lse2 : nullptr));
+  FLAREPP_TRY(decode(p, ws, q, 0, M * D, k, y, s, saved ? sv.lse2 : nullptr, c));
   return FLAREPP_OK;
 }
 
@@ -459,14 +443,9 @@ int flare_encode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
     if ((st = check_device()) != FLAREPP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float c = (float)((double)scale * 1.4426950408889634);
-    const int64_t qh = (int64_t)p.Mpad * D;
-    const bool per_batch = q_batch_stride != 0;
-    const size_t qoff = per_batch ? p.off_q : p.off_q0;
-    FLAREPP_TRY(prep_latents(p, workspace, qoff, q, q_batch_stride, (int)(per_batch ? B * H : H),
-                             c, s));
     FLAREPP_TRY(launch_encode(dtype, (int)D,
-                              encode_params(p, workspace, ws_at(workspace, qoff),
-                                            per_batch ? H * qh : 0, qh, k, v, nullptr),
+                              encode_params(p, workspace, q, q_batch_stride, M * D, k, v,
+                                            nullptr, c),
                               s));
     FLAREPP_TRY(value_operand(p, workspace, p.nchunks, nullptr, z, s));
     return FLAREPP_OK;
@@ -499,13 +478,8 @@ int flare_decode_fwd(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int 
     if ((st = check_device()) != FLAREPP_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float c = (float)((double)scale * 1.4426950408889634);
-    const int64_t qh = (int64_t)p.Mpad * D;
-    const bool per_batch = q_batch_stride != 0;
-    const size_t qoff = per_batch ? p.off_q : p.off_q0;
-    FLAREPP_TRY(prep_latents(p, workspace, qoff, q, q_batch_stride, (int)(per_batch ? B * H : H),
-                             c, s));
     FLAREPP_TRY(value_operand(p, workspace, 0, z, nullptr, s));
-    FLAREPP_TRY(decode(p, workspace, ws_at(workspace, qoff), per_batch ? H * qh : 0, qh, k, y, s));
+    FLAREPP_TRY(decode(p, workspace, q, q_batch_stride, M * D, k, y, s, nullptr, c));
     return FLAREPP_OK;
   } catch (...) {
     return FLAREPP_ERR_HIP;

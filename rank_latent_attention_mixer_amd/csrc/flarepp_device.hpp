@@ -135,6 +135,18 @@ __host__ __device__ __forceinline__ int value_row(int d) {
   return 8 * a + 4 * h + i;
 }
 
+// Eight consecutive latent elements as a scaled operand: (T)(s * x), each
+// rounded to nearest even -- the same bits as an operand copy formed
+// elementwise in fp32 beforehand.
+template <typename T>
+__device__ __forceinline__ u32x4 scaled8(const T* p, float s) {
+  const u32x4 raw = ldg16(p);
+  typename Pack8<T>::type x = bitcast_u4<typename Pack8<T>::type>(raw), y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (T)(s * (float)x[i]);
+  return to_u4(y);
+}
+
 // Logistic gate in fp32; -inf -> 0, +inf -> 1.
 __device__ __forceinline__ float gate_sigma(float g) {
   return 1.0f / (1.0f + expf(-g));

@@ -12,10 +12,12 @@ enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
 // Split-N encoder partials (synthesis and encode steps).
 struct EncodeParams {
-  const void* q;          // latent operand [.., Mpad, D] (dtype, or fp32 on the fp32
-                          // path), prescaled by scale*log2(e); padded rows are zero
+  const void* q;          // qscale == 0: latent operand [.., Mpad, D] (dtype, or fp32 on
+                          // the fp32 path), prescaled by scale*log2(e), padded rows zero;
+                          // qscale > 0: the caller's latents [.., M, D] unscaled
   int64_t q_b_stride;     // elements between batch elements (0 = shared)
   int64_t q_h_stride;     // elements between heads
+  float qscale;           // > 0: form the operand (dtype)(qscale * q) on load
   const void* k;          // [B, H, N, D]
   const void* v;          // [B, H, N, D]; may equal k
   int B, H;
@@ -63,8 +65,10 @@ enum { kOutNatural = 0, kOutValueT = 1, kOutNatural32 = 2 };
 
 // Decoder: y = softmax over latents of (k q^T) applied to z.
 struct DecodeParams {
-  const void* q;          // latent operand [.., Mpad, D] (prescaled)
+  const void* q;          // latent operand [.., Mpad, D] (prescaled), or with qscale > 0
+                          // the caller's latents [.., M, D] unscaled
   int64_t q_b_stride, q_h_stride;
+  float qscale;           // > 0: form the operand (dtype)(qscale * q) on load
   const void* zt;         // value operand: dtype [B*H][DV][Mpad] (slot order) or
                           // fp32 [B*H][Mpad][D] on the fp32 path
   const void* k;          // [B, H, N, D]
