@@ -312,6 +312,25 @@ def probe_peaks():
         t = start.elapsed_time(stop) / 20 / 1e3
         res[name] = lib.flarepp_probe_work(which, blocks, iters) / t
         log(f"[probe] {name}: {t * 1e3:.3f} ms per launch after {t_total:.2f} s")
+    # co-issue on one SIMD (four waves per SIMD): time per wave-iteration of
+    # 4 products alone, 32 three-source FMAs alone, and both interleaved
+    co = {}
+    for which, name in ((4, "mfma"), (5, "fma"), (6, "mix")):
+        for _ in range(2):
+            lib.flarepp_probe_launch(which, blocks, iters, ctypes.c_void_p(out.data_ptr()), stream)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(10):
+            lib.flarepp_probe_launch(which, blocks, iters, ctypes.c_void_p(out.data_ptr()), stream)
+        stop.record()
+        torch.cuda.synchronize()
+        t = start.elapsed_time(stop) / 10 / 1e3
+        # ns per wave-iteration on one SIMD (1024 SIMDs share the launch)
+        co[name] = t * 1e9 * 1024 / lib.flarepp_probe_work(which, blocks, iters)
+        log(f"[probe] co-issue {name}: {co[name]:.2f} ns per wave-iteration per SIMD")
+    hidden = (co["mfma"] + co["fma"] - co["mix"]) / co["fma"]
     from flarepp_workloads import WORKLOADS
     w = WORKLOADS["million_token_bf16"]
     exps = 3 * w.B * w.H * w.N * w.M  # one forward, every gate open
@@ -323,6 +342,8 @@ def probe_peaks():
         "exp_ms_per_million_token_forward": float(f"{exps / res['exp_f32'] * 1e3:.4g}"),
         "mfma_bf16_tflops_sustained_random_operands": round(res["mfma_bf16_random_sustained"] / 1e12, 1),
         "mfma_bf16_tflops_sustained_ones_operands": round(res["mfma_bf16_ones_sustained"] / 1e12, 1),
+        "coissue_ns_per_wave_iteration": {k: round(v, 2) for k, v in co.items()},
+        "coissue_fma_share_hidden_by_mfma": round(hidden, 3),
     }), flush=True)
     return 0
 

@@ -16,12 +16,19 @@ extern "C" {
  * MFMA_BF16_RANDOM / MFMA_BF16_ONES: the same products with operands of
  * random sign and mantissa, or all 1.0 -- run for a second or more, the
  * pair shows how far the power limit lowers the clock when operand bits
- * toggle as real data does. */
+ * toggle as real data does.
+ * COISSUE_MFMA / COISSUE_FMA / COISSUE_MIX: per iteration four independent
+ * 32x32x16 products, 32 independent three-source fp32 FMAs, or both
+ * interleaved (eight FMAs after each product) -- the three times give the
+ * share of vector-ALU time the matrix cores hide on one SIMD. */
 enum {
   FLAREPP_PROBE_MFMA_BF16 = 0,
   FLAREPP_PROBE_EXP_F32 = 1,
   FLAREPP_PROBE_MFMA_BF16_RANDOM = 2,
-  FLAREPP_PROBE_MFMA_BF16_ONES = 3
+  FLAREPP_PROBE_MFMA_BF16_ONES = 3,
+  FLAREPP_PROBE_COISSUE_MFMA = 4,
+  FLAREPP_PROBE_COISSUE_FMA = 5,
+  FLAREPP_PROBE_COISSUE_MIX = 6
 };
 
 /* Launches probe `which` with `blocks` workgroups of 256 threads, each lane
@@ -30,7 +37,8 @@ enum {
  * for a launch error.  Asynchronous on `stream`. */
 int flarepp_probe_launch(int which, int blocks, int iters, float* out, void* stream);
 
-/* Work done by one such launch: flops (MFMA probe) or exponentials. */
+/* Work done by one such launch: flops (MFMA probes), exponentials, or
+ * wave-iterations (co-issue probes). */
 double flarepp_probe_work(int which, int blocks, int iters);
 
 #ifdef __cplusplus
