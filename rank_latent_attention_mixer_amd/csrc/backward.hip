@@ -394,7 +394,12 @@ __global__ __launch_bounds__(64 * lat_waves<D>()) void bwd_lat_kernel(BwdLatPara
         ops.rows(base + GI * TB, g, gk);
         gg = product<V8, KD>(gk, gop, DEC ? lds_rowvec(tvec[cur][1], g, h) : cg);
       }
-      if (kvalid < 32) mask_slots(s, kvalid, h);
+      if (kvalid < 32) {  // block-uniform; only a chunk's last group
+        // an empty volatile asm keeps this a branch: if-converted into
+        // selects it would cost ~45 VALU instructions on every group
+        asm volatile("");
+        mask_slots(s, kvalid, h);
+      }
       float p[16], t[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -449,9 +454,15 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
   using L = RowLayout<D>;
   constexpr int KD = O::KD, NDB = O::NDB;
   constexpr bool DEC = MODE == kBwdTokFlare;  // decoder terms (P2, G1)
-  // LDS: latent tensors 0 (score rows, Y columns), 1 (G1 rows), 2 (G2 rows,
-  // X columns), then the per-latent C vectors of P1 and G2
+  // LDS, one block per group of 32 latents: the group's rows of latent
+  // tensors 0 (score rows, Y columns), 1 (G1 rows) and 2 (G2 rows, X
+  // columns), then its 32 entries of the per-latent vectors (C of P1, C of
+  // G2, the fast form's U).  Every read of a group is one lane address plus
+  // a compile-time offset from the group's base.
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  constexpr int kTen = 32 * L::ROWB;        // one tensor's rows of a group
+  constexpr int kVec = 3 * kTen;            // the group's vectors, 3 x 32 floats
+  constexpr int kGrp = kVec + 3 * 32 * 4;   // bytes per group
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
@@ -463,8 +474,10 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
   const bool closed = a.gate != nullptr && gate_sigma(a.gate[hd]) == 0.f;
 
   const int Mk = (a.M + 31) & ~31;
-  const int TB = Mk * L::ROWB;
-  float* vec = reinterpret_cast<float*>(lds_raw + 3 * TB);   // [3][Mk]
+  // per-latent vector j, entry m
+  auto vec_at = [&](int j, int m) -> float& {
+    return *reinterpret_cast<float*>(lds_raw + (m >> 5) * kGrp + kVec + 128 * j + 4 * (m & 31));
+  };
   // FLARE part, fast form: P2 = P1 U[m] W[n] with U = 2^(lse1 - shift - Ls)
   // and W = 2^(Ls - lse2 - e) (the two weights share their score; Ls, the
   // largest lse1 - shift of the range, keeps U <= 1), one exponential per
@@ -485,15 +498,16 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
         const int row = e / L::CPR, c = e - row * L::CPR;
         const u32x4 v = row < a.M ? ldg16(src + ((int64_t)row * D + 8 * c) * 2)
                                   : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&lds_raw[t * TB + L::offset(row, 16 * c)]) = v;
+        *reinterpret_cast<u32x4*>(&lds_raw[(row >> 5) * kGrp + t * kTen +
+                                           L::offset(row & 31, 16 * c)]) = v;
       }
     }
     float lmax = -__builtin_inff(), tmin = __builtin_inff();
     for (int m = tid; m < Mk; m += 64 * NWV) {
       const bool in = m < a.M;
       const int64_t i = (int64_t)set * (a.lat_stat_stride ? a.lat_stat_stride : a.M) + m;
-      vec[m] = in ? a.shift - a.lat_lse[i] : 0.f;
-      vec[Mk + m] = in ? a.lat_negd[i] : 0.f;
+      vec_at(0, m) = in ? a.shift - a.lat_lse[i] : 0.f;
+      vec_at(1, m) = in ? a.lat_negd[i] : 0.f;
       if (in) lmax = fmaxf(lmax, a.lat_lse[i]);
     }
     if constexpr (kFastForm) {
@@ -524,13 +538,10 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
              fabsf(Ls) <= 1e30f;
       if (fast)
         for (int m = tid; m < Mk; m += 64 * NWV)
-          vec[2 * Mk + m] = m < a.M ? __builtin_amdgcn_exp2f(-vec[m] - Ls) : 0.f;
+          vec_at(2, m) = m < a.M ? __builtin_amdgcn_exp2f(-vec_at(0, m) - Ls) : 0.f;
     }
   }
   __syncthreads();
-  const unsigned char* lat0 = lds_raw;
-  const unsigned char* lat1 = lds_raw + TB;
-  const unsigned char* lat2 = lds_raw + 2 * TB;
   const int nfull = a.M / 32, mtail = a.M - 32 * nfull;
 
   O ops;
@@ -575,16 +586,18 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
     // compile-time variant, so full groups carry no selects
     auto group = [&](int G, int kvalid, auto tail, auto fast_form) {
       constexpr bool FAST = decltype(fast_form)::value;
+      const unsigned char* gb = lds_raw + G * kGrp;
+      const float* gv = reinterpret_cast<const float*>(gb + kVec);
       V8 lop[KD];
-      ops.rows(lat0, G, lop);
-      f32x16 s1 = product<V8, KD>(lop, kop, lds_rowvec(vec, G, h));
+      ops.rows(gb, 0, lop);
+      f32x16 s1 = product<V8, KD>(lop, kop, lds_rowvec(gv, 0, h));
       f32x16 s2 = splat16(0.f);
       if constexpr (DEC && !FAST) s2 = product<V8, KD>(lop, kop, cs2);
-      ops.rows(lat2, G, lop);
-      const f32x16 g2 = product<V8, KD>(lop, b2, lds_rowvec(vec + Mk, G, h));
+      ops.rows(gb + 2 * kTen, 0, lop);
+      const f32x16 g2 = product<V8, KD>(lop, b2, lds_rowvec(gv + 32, 0, h));
       f32x16 g1 = splat16(0.f);
       if constexpr (DEC) {
-        ops.rows(lat1, G, lop);
+        ops.rows(gb + kTen, 0, lop);
         g1 = product<V8, KD>(lop, b1, cg1);
       }
       if constexpr (decltype(tail)::value) {
@@ -594,7 +607,7 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
       float p[16], t[16];
       if constexpr (FAST) {
         // T = P1 (G2 + U W G1)
-        const f32x16 u = lds_rowvec(vec + 2 * Mk, G, h);
+        const f32x16 u = lds_rowvec(gv + 64, 0, h);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           p[v] = __builtin_amdgcn_exp2f(s1[v]);
@@ -612,9 +625,9 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
       pack16<T>(t, Tm);
       pack16<T>(p, P);
       V8 va[NDB][2];
-      ops.cols(lat0, G, va);
+      ops.cols(gb, 0, va);
       accumulate<V8, NDB>(y, va, Tm);
-      ops.cols(lat2, G, va);
+      ops.cols(gb + 2 * kTen, 0, va);
       accumulate<V8, NDB>(x, va, P);
     };
     if constexpr (D == 64) {  // one code path (a second one spills at this width)
