@@ -394,12 +394,7 @@ __global__ __launch_bounds__(64 * lat_waves<D>()) void bwd_lat_kernel(BwdLatPara
         ops.rows(base + GI * TB, g, gk);
         gg = product<V8, KD>(gk, gop, DEC ? lds_rowvec(tvec[cur][1], g, h) : cg);
       }
-      if (kvalid < 32) {  // block-uniform; only a chunk's last group
-        // an empty volatile asm keeps this a branch: if-converted into
-        // selects it would cost ~45 VALU instructions on every group
-        asm volatile("");
-        mask_slots(s, kvalid, h);
-      }
+      if (kvalid < 32) mask_slots(s, kvalid, h);
       float p[16], t[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
