@@ -55,6 +55,10 @@ PAGES_CONTEXT = {
 }
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+# fp32 vector, published: 256 CUs x 4 SIMDs x 16 lanes x 2 flops per FMA x 2
+# (packed two-wide FMA) x 2.4 GHz; kernels built without packed fp32
+# instructions issue at most half of it
+PEAK_FP32_VECTOR_TFLOPS = 157.3
 # kernel i of a forward runs between timing events i + 1 and i + 2 (events 0
 # and 1 are recorded back to back: the seeds need no launch of their own)
 KERNELS = ["encode_synthesis", "combine_query", "encode", "combine_value", "decode"]
@@ -520,8 +524,10 @@ def main(argv=None):
     dur = per_kernel[dom] / 1e3
     achieved = f_launch / dur / 1e12
     traffic = read_traffic(TRAFFIC_FILE, w.name, dom)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+    # fp32 runs the vector-ALU kernels: their bound is the fp32 vector rate
+    bound, peak = ("alu", PEAK_FP32_VECTOR_TFLOPS) if w.dtype == "fp32" else ("mfma", PEAK_BF16_TFLOPS)
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel": dom,
                 "algorithmic_flops_per_launch": f_launch,
                 "algorithmic_bytes_per_launch": b_launch,
