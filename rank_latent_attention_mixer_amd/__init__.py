@@ -62,7 +62,9 @@ class FlareppError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_PKG, "libflarepp.so")
+    """The in-tree libflarepp.so, or the file FLAREPP_LIBRARY names (the host
+    sanitizer test points it at an instrumented build of the same sources)."""
+    return os.environ.get("FLAREPP_LIBRARY") or os.path.join(_PKG, "libflarepp.so")
 
 
 def load_library():

@@ -55,16 +55,19 @@ struct Saved {
   float *q, *z, *qd, *lse0, *lse1, *lse2;
   size_t floats;
 };
+// base may be null (a forward that saves nothing): then every slot is null
+// and only `floats` is meaningful (no arithmetic on a null pointer)
 inline Saved saved_layout(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, float* base) {
   Saved v;
   const size_t lat = (size_t)(B * H * M * D), row = (size_t)(B * H * M);
   size_t o = 0;
-  v.q = base + o; o += lat;
-  v.z = base + o; o += lat;
-  v.qd = base + o; o += lat;
-  v.lse0 = base + o; o += row;
-  v.lse1 = base + o; o += row;
-  v.lse2 = base + o; o += (size_t)(B * H * N);
+  auto at = [base](size_t off) { return base ? base + off : nullptr; };
+  v.q = at(o); o += lat;
+  v.z = at(o); o += lat;
+  v.qd = at(o); o += lat;
+  v.lse0 = at(o); o += row;
+  v.lse1 = at(o); o += row;
+  v.lse2 = at(o); o += (size_t)(B * H * N);
   v.floats = o;
   return v;
 }
