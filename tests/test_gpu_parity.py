@@ -168,6 +168,21 @@ def test_gate_special_values(fp, dtype):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_gate_nan_propagates(fp, dtype):
+    """A NaN gate logit makes its head's output NaN (sigma(NaN) times the
+    synthesis); every other head matches the oracle."""
+    x = make_random_inputs(2, 3, 300, 48, 16, dtype, seed=78, gate=[0.4, math.nan, -math.inf])
+    y = run_mixer(fp, x, dtype)
+    assert np.all(np.isnan(y[:, 1]))
+    for h in (0, 2):
+        ref = oracle.flarepp_ref(**f64({n: (x[n][h:h + 1] if n in ("q0", "q_fixed", "gate")
+                                             else x[n][:, h:h + 1]) for n in NAMES}))
+        err = rel_err(y[:, h:h + 1], ref)
+        note(f"[gate-nan] {dtype} head {h} rel err {err:.3e}")
+        assert err <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_gate_closed_equals_flare_bitwise(fp, dtype):
     x = make_random_inputs(2, 3, 2000, 64, 32, dtype, seed=5, gate=-math.inf)

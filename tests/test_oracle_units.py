@@ -65,6 +65,21 @@ def test_gate_sigma_pin():
     assert _rel(got, want) <= 1e-15
 
 
+def test_nan_gate_propagates_to_its_head_only():
+    """A NaN gate logit gives a NaN routing query for its head, so that
+    head's output is NaN; the other heads are the ones of a finite gate."""
+    r = _rng(31)
+    B, H, N, M, D = 1, 3, 40, 6, 4
+    x = dict(q0=r.standard_normal((H, M, D)), q_fixed=r.standard_normal((H, M, D)),
+             gate=np.array([0.4, np.nan, -np.inf]), k0=r.standard_normal((B, H, N, D)),
+             k=r.standard_normal((B, H, N, D)), v=r.standard_normal((B, H, N, D)))
+    y = oracle.flarepp_ref(**x)
+    assert np.all(np.isnan(y[:, 1]))
+    finite = dict(x, gate=np.array([0.4, 0.0, -np.inf]))
+    y_ok = oracle.flarepp_ref(**finite)
+    assert np.array_equal(y[:, 0], y_ok[:, 0]) and np.array_equal(y[:, 2], y_ok[:, 2])
+
+
 def test_attention_matrix_pin():
     r = _rng(11)
     q, k = r.standard_normal((7, 5)), r.standard_normal((13, 5))
