@@ -10,6 +10,9 @@
 // latents 32 at a time with the shared online-softmax tile, and writes its
 // normalised y rows.  The value operand arrives with permuted rows so that
 // each lane holds 4*NDB contiguous output columns of one token.
+#include <type_traits>
+#include <utility>
+
 #include "flash_tile.hpp"
 #include "kernels.hpp"
 
@@ -31,20 +34,45 @@ struct DecodeWaves {
   static constexpr int value = D >= 64 ? 8 : FLAREPP_DEC_WAVES;
 };
 
+constexpr int kMaxLdsBytes = 160 * 1024;
+
+// f(integral_constant<K>) for K = 0, 1, ... in order while each returns true
+template <int... K, typename F>
+__device__ __forceinline__ bool all_slots(std::integer_sequence<int, K...>, F& f) {
+  return (f(std::integral_constant<int, K>{}) && ...);
+}
+
+// LDS: the resident latents, then (STAGE) one staging tile per wave of its
+// 32 * kNC token rows at pitch SP.  A staged wave reads and writes HBM one
+// contiguous KiB per instruction and moves the rows into (and the outputs
+// out of) the matrix-core layout through its staging tile; unstaged, each
+// lane reads and writes 16-byte pieces of its own token's row, 32 rows per
+// instruction.  At D = 64 a row is 128 bytes and the unstaged pattern holds
+// the decoder well below the HBM rate of a plain copy; at D <= 32 the
+// decoder is bound by its arithmetic and is not staged.
 template <int D>
 struct DecodeLds {
   static constexpr int DV = D < 32 ? 32 : D;
   static constexpr int KP = D + 8;  // latent row pitch (elements)
+  static constexpr int SP = D + 8;  // staging row pitch (elements)
+  static constexpr int kStageElems = DecodeWaves<D>::value * 32 * kNC * SP;
   static int zpitch(int Mk) { return Mk + 8; }
-  static int elems(int Mk) { return Mk * KP + DV * zpitch(Mk); }
+  static int elems(int Mk, bool stage) {
+    return Mk * KP + DV * zpitch(Mk) + (stage ? kStageElems : 0);
+  }
+  // staged when the staging tiles fit beside the resident latents
+  static bool stage(int Mk) { return D >= 64 && elems(Mk, true) * 2 <= kMaxLdsBytes; }
 };
 
 // FIXUP = false: the decoder proper; a wave whose sums leave the fixed
-// reference's range records that tile instead of storing it.
+// reference's range records that tile (its stores still go out and are
+// overwritten later).
 // FIXUP = true: the same workgroups again, recomputing only the recorded
 // tiles by the exact two-pass method (a workgroup with none exits at once).
 // The split keeps the rare exact path's registers out of the main kernel.
-template <typename T, int D, bool FIXUP>
+// LSE: also store each token's log2 row sum plus reference (training).
+// STAGE: token rows and outputs pass through a per-wave LDS staging tile.
+template <typename T, int D, bool FIXUP, bool LSE, bool STAGE>
 __global__ __launch_bounds__(64 * DecodeWaves<D>::value) void
 decode_kernel(DecodeParams a) {
   constexpr int kNW = DecodeWaves<D>::value;
@@ -53,6 +81,8 @@ decode_kernel(DecodeParams a) {
   using V8 = typename Tile::V8;
   constexpr int KD = Tile::KD, DV = Tile::DV, NDB = Tile::NDB;
   constexpr int KP = DecodeLds<D>::KP;
+  constexpr int SP = DecodeLds<D>::SP;
+  static_assert(!STAGE || D >= 16, "staging moves whole 16-byte pieces of rows");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   T* qs = reinterpret_cast<T*>(lds_raw);
 
@@ -66,6 +96,13 @@ decode_kernel(DecodeParams a) {
   const int bh = blockIdx.x / a.wg_per_bh;
   const int part = blockIdx.x - bh * a.wg_per_bh;
   const int b = bh / a.H, hd = bh - b * a.H;
+  // this wave's staging tile (STAGE): rows cb * 32 + j, pitch SP
+  T* sg = zs + DV * ZP + wave * (32 * kNC * SP);
+  // staged HBM access: instruction i of a 32-row block moves its bytes
+  // [1024 i, 1024 i + 1024); lane l's 16 bytes are row i * kRPI + l / kCPR,
+  // elements 8 (l % kCPR) .. +7
+  constexpr int kCPR = D / 8, kRPI = 64 / kCPR;
+  const int srow = lane / kCPR, scol = 8 * (lane % kCPR);
 
   // this wave's record: bit i = the workgroup's i-th tile (i < 64), and
   // 1 + the first ordinal >= 64 from which every tile is recomputed (0: none)
@@ -152,12 +189,24 @@ decode_kernel(DecodeParams a) {
             *reinterpret_cast<const V8*>(zsb + vl[db] + G * VSTEP + kk * 16 * (int)sizeof(T));
   };
 
-  // token rows of one tile for this wave, as the register-side operand.
-  // Rows past N re-read row N-1 (their outputs are never stored; every token
-  // column is independent), so the loads carry no condition and the
-  // compiler can wait for exactly the loads a tile needs.
+  // token rows of one tile for this wave: unstaged, already the
+  // register-side operand; staged, the rows as they lie in HBM (to_operand
+  // rearranges them).  Rows past N re-read row N-1 (every token column is
+  // independent, and such a column's outputs equal row N-1's), so the loads
+  // carry no condition and the compiler can wait for exactly the loads a
+  // tile needs.
   auto load_tokens = [&](int64_t tile, V8 (&dst)[kNC][KD]) {
     const int64_t nb = tile * kTokTile + wave * 32 * kNC;
+    if constexpr (STAGE) {
+#pragma unroll
+      for (int cb = 0; cb < kNC; ++cb)
+#pragma unroll
+        for (int i = 0; i < KD; ++i) {
+          const int64_t n = min(nb + cb * 32 + i * kRPI + srow, a.N - 1);
+          dst[cb][i] = bitcast_u4<V8>(ldg16(kg + n * D + scol));
+        }
+      return;
+    }
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
       const int64_t n = min(nb + cb * 32 + r, a.N - 1);
@@ -174,31 +223,64 @@ decode_kernel(DecodeParams a) {
     }
   };
 
-// y = O / l; lane (h, r) owns columns 32db + 16h .. +15 of token r
+  // register-side operand of a tile from what load_tokens fetched
+  auto to_operand = [&](const V8 (&src)[kNC][KD], V8 (&q)[kNC][KD]) {
+    if constexpr (STAGE) {
+#pragma unroll
+      for (int cb = 0; cb < kNC; ++cb)
+#pragma unroll
+        for (int i = 0; i < KD; ++i)
+          *reinterpret_cast<V8*>(sg + (cb * 32 + i * kRPI + srow) * SP + scol) = src[cb][i];
+#pragma unroll
+      for (int cb = 0; cb < kNC; ++cb)
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd)
+          q[cb][kd] = *reinterpret_cast<const V8*>(sg + (cb * 32 + r) * SP + 16 * kd + 8 * h);
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < kNC; ++cb)
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd) q[cb][kd] = src[cb][kd];
+    }
+  };
+
+// y = O / l; lane (h, r) owns columns 32db + 16h .. +15 of token r (staged:
+// they go to the staging tile and leave it a contiguous KiB per store).
+// Every lane stores, so the number of stores per tile is fixed and the
+// waits before a tile count only its own loads (a conditional store would
+// make the compiler also wait for the previous tile's stores).  A column
+// past N holds row N-1's inputs and so exactly row N-1's results: it
+// stores them to row N-1 again.
 auto store_tile = [&](int64_t nb, const auto& t) {
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
       const float l = t.row_sum(cb);
       const float inv = 1.0f / l;
-      const int64_t n = nb + cb * 32 + r;
-      if (a.lse_out && h == 0 && n < a.N)  // saved for the backward pass
+      const int64_t n = min(nb + cb * 32 + r, a.N - 1);
+      if constexpr (LSE)  // both halves of the wave hold token r's sum
         a.lse_out[(int64_t)bh * a.N + n] = log2f(l) + t.reference(cb);
-      if (n < a.N) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d0 = 32 * db + 16 * h;
-          if (d0 < D) {
-            T out[16];
+      for (int db = 0; db < NDB; ++db) {
+        const int d0 = 32 * db + 16 * h;
+        if (d0 < D) {  // lane-dependent only for D < 32
+          T out[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) out[v] = (T)(t.o[db][cb][v] * inv);
-            T* dst = yg + n * D + d0;
-            if constexpr (D >= 16) {
-              *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
-              *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(&out[8]);
-            } else {
-              *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
-            }
+          for (int v = 0; v < 16; ++v) out[v] = (T)(t.o[db][cb][v] * inv);
+          T* dst = STAGE ? sg + (cb * 32 + r) * SP + d0 : yg + n * D + d0;
+          if constexpr (D >= 16) {
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
+            *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(&out[8]);
+          } else {
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
           }
+        }
+      }
+      if constexpr (STAGE) {
+#pragma unroll
+        for (int i = 0; i < KD; ++i) {
+          const int row = i * kRPI + srow;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sg + (cb * 32 + row) * SP + scol);
+          *reinterpret_cast<u32x4*>(yg + min(nb + cb * 32 + row, a.N - 1) * D + scol) = v;
         }
       }
     }
@@ -206,16 +288,16 @@ auto store_tile = [&](int64_t nb, const auto& t) {
 
   // One tile: the wave's 32 * kNC token rows arrive as qop (register
   // operand); sweep all latents and store y.  Returns true when the fixed
-  // reference failed (nothing stored; the tile needs the exact path).
-  auto process_tile = [&](int64_t tile, const V8 (&qop)[kNC][KD]) -> bool {
+  // reference failed: what was stored is then wrong and the fix-up pass
+  // recomputes the tile.  A wave whose rows all lie past N (last tile of a
+  // ragged N) computes row N-1 and stores it again, which keeps the store
+  // count free of branches.
+  auto process_tile = [&](int64_t tile, const V8 (&qop)[kNC][KD])
+                          __attribute__((always_inline)) -> bool {
     const int64_t nb = tile * kTokTile + wave * 32 * kNC;
-    if (nb >= a.N) return false;  // wave-uniform; no barrier below
     Tile st;
     st.reset();
-#pragma unroll
-    for (int cb = 0; cb < kNC; ++cb)
-#pragma unroll
-      for (int kd = 0; kd < KD; ++kd) st.q[cb][kd] = qop[cb][kd];
+    to_operand(qop, st.q);
     // latent groups of 32: group 0, then full groups as a two-stage
     // pipeline (the score product of group G+1 is issued before the
     // softmax of group G, two score buffers alternating), then a masked
@@ -276,9 +358,9 @@ auto store_tile = [&](int64_t nb, const auto& t) {
       vop_at(nfull, vop);
       st.template next<true>(sa, vop, mtail, h);
     }
-    if (st.overflowed_bounded(zmax)) return true;  // recomputed exactly in the fix-up pass
+    const bool bad = st.overflowed_bounded(zmax);  // recomputed exactly in the fix-up pass
     store_tile(nb, st);
-    return false;
+    return bad;
   };
 
   // Sums out of range for the fixed reference: exact two-pass recompute of
@@ -290,10 +372,7 @@ auto store_tile = [&](int64_t nb, const auto& t) {
     using Exact = FlashTile<T, D, kNC, true>;
     Exact ex;
     ex.reset();
-#pragma unroll
-    for (int cb = 0; cb < kNC; ++cb)
-#pragma unroll
-      for (int kd = 0; kd < KD; ++kd) ex.q[cb][kd] = qop[cb][kd];
+    to_operand(qop, ex.q);
     const int ngrp = nfull + (mtail > 0 ? 1 : 0);
     f32x16 sa[kNC];
     float mx[kNC];
@@ -322,10 +401,11 @@ auto store_tile = [&](int64_t nb, const auto& t) {
   };
 
   // The workgroup walks tiles part, part + wg_per_bh, ...; the token rows of
-  // the next tile are fetched into the other of two register sets while the
-  // current tile is computed (the loop is unrolled by two so the sets never
-  // need copying).
-  V8 qa[kNC][KD], qb[kNC][KD];
+  // the next kDepth - 1 tiles are in flight in a ring of register sets while
+  // the current tile is computed (the loop is unrolled by kDepth so the sets
+  // never need copying).  Two tiles in flight measured no faster than one.
+  constexpr int kDepth = 2;
+  V8 ring[kDepth][kNC][KD];
   if constexpr (!FIXUP) {
     // Tiles that overflowed are remembered by their ordinal i among this
     // workgroup's tiles (bit i of a mask for i < 64; past that, every tile
@@ -336,20 +416,37 @@ auto store_tile = [&](int64_t nb, const auto& t) {
       if (i < 64) bad |= (uint64_t)1 << i;
       else if (bad_from < 0) bad_from = i;
     };
+    const int64_t step = a.wg_per_bh;
     int64_t tile = part, ord = 0;
-    load_tokens(tile, qa);
-    while (tile < ntiles) {
-      // issued even past the last tile (rows clamp to N-1, results unused):
-      // no branch, so the waits before each tile count exactly its own loads
-      const int64_t t1 = tile + a.wg_per_bh;
-      load_tokens(t1, qb);
-      if (process_tile(tile, qa)) note_bad(ord);
-      if (t1 >= ntiles) break;
-      const int64_t t2 = t1 + a.wg_per_bh;
-      load_tokens(t2, qa);
-      if (process_tile(t1, qb)) note_bad(ord + 1);
-      tile = t2;
-      ord += 2;
+    // Prologue: the first kDepth - 1 ring slots, each load followed by as
+    // many store instructions as a tile issues (single bytes to distinct
+    // places of this wave's record, which is written in full after the
+    // loop).  The loop is then entered with the same memory-counter history
+    // as from its back edge, and the compiler's wait before every tile
+    // counts only that tile's loads, never the stores of the tiles before.
+    constexpr int kTileStores = kNC * ((STAGE ? KD : NDB * (D >= 16 ? 2 : 1)) + (LSE ? 1 : 0));
+    static_assert(2 * kTileStores <= 16, "record too small for the prologue stores");
+    unsigned char* pad = reinterpret_cast<unsigned char*>(rec);
+#pragma unroll
+    for (int k = 0; k + 1 < kDepth; ++k) {
+      load_tokens(tile + k * step, ring[k]);
+#pragma unroll
+      for (int j = 0; j < kTileStores; ++j) pad[2 * j] = (unsigned char)k;
+    }
+    // one tile on ring slot K; false once the walk is over.  The loop below
+    // has a single exit, so its header is reached only from the prologue and
+    // from its back edge.
+    auto slot = [&](auto kc) __attribute__((always_inline)) -> bool {
+      constexpr int K = decltype(kc)::value;
+      if (tile >= ntiles) return false;
+      // issued even past the last tile (rows clamp to N-1, results unused)
+      load_tokens(tile + (kDepth - 1) * step, ring[(K + kDepth - 1) % kDepth]);
+      if (process_tile(tile, ring[K])) note_bad(ord);
+      tile += step;
+      ++ord;
+      return true;
+    };
+    while (all_slots(std::make_integer_sequence<int, kDepth>{}, slot)) {
     }
     if (lane == 0) {  // written for every wave, so no clearing is needed
       rec[0] = bad;
@@ -361,8 +458,8 @@ auto store_tile = [&](int64_t nb, const auto& t) {
       const bool redo =
           ord < 64 ? ((fx_bad >> ord) & 1) != 0 : (fx_from >= 0 && ord >= fx_from);
       if (!redo) continue;
-      load_tokens(t, qa);
-      exact_tile(t, qa);
+      load_tokens(t, ring[0]);
+      exact_tile(t, ring[0]);
     }
   }
 }
@@ -434,30 +531,38 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams a) {
   }
 }
 
-template <typename T, int D>
-hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
+template <typename T, int D, bool LSE, bool STAGE>
+hipError_t launch_mfma_s(const DecodeParams& p, hipStream_t s) {
   const int Mk = (p.M + 31) & ~31;
-  const size_t lds = (size_t)DecodeLds<D>::elems(Mk) * sizeof(T);
+  const size_t lds = (size_t)DecodeLds<D>::elems(Mk, STAGE) * sizeof(T);
   if (lds > 64 * 1024) {
-    for (const void* f : {(const void*)decode_kernel<T, D, false>,
-                          (const void*)decode_kernel<T, D, true>}) {
+    for (const void* f : {(const void*)decode_kernel<T, D, false, LSE, STAGE>,
+                          (const void*)decode_kernel<T, D, true, LSE, STAGE>}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
   }
   const dim3 grid((unsigned)(p.B * p.H * p.wg_per_bh)), block(64 * DecodeWaves<D>::value);
-  hipLaunchKernelGGL((decode_kernel<T, D, false>), grid, block, lds, s, p);
-  hipLaunchKernelGGL((decode_kernel<T, D, true>), grid, block, lds, s, p);
+  hipLaunchKernelGGL((decode_kernel<T, D, false, LSE, STAGE>), grid, block, lds, s, p);
+  hipLaunchKernelGGL((decode_kernel<T, D, true, LSE, STAGE>), grid, block, lds, s, p);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int D, bool LSE>
+hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
+  if constexpr (D >= 64) {
+    if (DecodeLds<D>::stage((p.M + 31) & ~31)) return launch_mfma_s<T, D, LSE, true>(p, s);
+  }
+  return launch_mfma_s<T, D, LSE, false>(p, s);
+}
+
+template <typename T, bool LSE>
 hipError_t launch_mfma_d(int D, const DecodeParams& p, hipStream_t s) {
   switch (D) {
-    case 8: return launch_mfma<T, 8>(p, s);
-    case 16: return launch_mfma<T, 16>(p, s);
-    case 32: return launch_mfma<T, 32>(p, s);
-    case 64: return launch_mfma<T, 64>(p, s);
+    case 8: return launch_mfma<T, 8, LSE>(p, s);
+    case 16: return launch_mfma<T, 16, LSE>(p, s);
+    case 32: return launch_mfma<T, 32, LSE>(p, s);
+    case 64: return launch_mfma<T, 64, LSE>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -483,17 +588,20 @@ int decode_lds_bytes(int M, int D, int dtype) {
   if (dtype == kF32) return 0;
   const int Mk = (M + 31) & ~31;
   switch (D) {
-    case 8: return DecodeLds<8>::elems(Mk) * 2;
-    case 16: return DecodeLds<16>::elems(Mk) * 2;
-    case 32: return DecodeLds<32>::elems(Mk) * 2;
-    case 64: return DecodeLds<64>::elems(Mk) * 2;
+    case 8: return DecodeLds<8>::elems(Mk, false) * 2;
+    case 16: return DecodeLds<16>::elems(Mk, false) * 2;
+    case 32: return DecodeLds<32>::elems(Mk, false) * 2;
+    case 64: return DecodeLds<64>::elems(Mk, DecodeLds<64>::stage(Mk)) * 2;
     default: return -1;
   }
 }
 
 hipError_t launch_decode(int dtype, int D, const DecodeParams& p, hipStream_t s) {
-  if (dtype == kBF16) return launch_mfma_d<__bf16>(D, p, s);
-  if (dtype == kF16) return launch_mfma_d<_Float16>(D, p, s);
+  const bool lse = p.lse_out != nullptr;
+  if (dtype == kBF16)
+    return lse ? launch_mfma_d<__bf16, true>(D, p, s) : launch_mfma_d<__bf16, false>(D, p, s);
+  if (dtype == kF16)
+    return lse ? launch_mfma_d<_Float16, true>(D, p, s) : launch_mfma_d<_Float16, false>(D, p, s);
   switch (D) {
     case 8: return launch_f32<8>(p, s);
     case 16: return launch_f32<16>(p, s);
