@@ -7,11 +7,17 @@ M=512, D=32, bf16, seeded synthetic inputs already resident in HBM).  The
 timed region is exactly K plain calls; the per-kernel split comes from K
 further calls with HIP events between the launches.
 Prints one JSON line on stdout; progress goes to stderr.
+Without --warmup the warm-up runs for at least WARMUP_SECONDS (and at
+least 5 steps), so that the GPU has reached the clock it sustains under the
+work before the timed region: a few milliseconds of warm-up measure a
+still-ramping clock, up to 20% slower at the smaller workloads.  The JSON
+line reports the number of warm-up steps run.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--cpu-seconds S | --no-cpu-baseline]
   python bench.py --copy-calibration-mib S   (plain device copy of S MiB, for
-                                              scaling the HBM byte counters)
+                                              scaling the HBM byte counters;
+                                              then 20 more copies timed)
   python bench.py --backward [--steps K] [--warmup W] [--workload NAME]
                   (times flarepp_mixer_bwd alone: one training forward fills
                    the saved tensors, then K backward calls are timed)
@@ -145,8 +151,9 @@ def read_traffic(path, workload, kernel, digest=None):
 
 
 def copy_calibration(mib):
-    """Times nothing: issues 5 plain device-to-device copies of `mib` MiB so
-    that a counter run can relate FETCH_SIZE / WRITE_SIZE to known bytes."""
+    """Issues 5 plain device-to-device copies of `mib` MiB so that a counter
+    run can relate FETCH_SIZE / WRITE_SIZE to known bytes (every copy of the
+    run moves the same bytes), then times 20 more."""
     import torch
     n = mib * (1 << 20) // 4
     src = torch.rand(n, device="cuda:0")
@@ -155,8 +162,23 @@ def copy_calibration(mib):
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "copies": 5}),
-          flush=True)
+    # then the same copy timed on its own (after a time-based warm-up), as
+    # the HBM rate a plain read-and-write stream reaches on this device
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < WARMUP_SECONDS:
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(20):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / 20
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "copies": 5,
+                      "timed_copy_ms": round(ms, 4),
+                      "timed_copy_GBs": round(2 * n * 4 / (ms / 1e3) / 1e9, 1)}), flush=True)
     return 0
 
 
@@ -173,6 +195,26 @@ def algorithmic_work(w, sig_open):
         "encode": (per_head_flops * w.H, 2 * per_head_bytes * w.H),                # k, v
         "decode": (per_head_flops * w.H, 2 * per_head_bytes * w.H),                # k in, y out
     }
+
+
+WARMUP_SECONDS = 0.5
+
+
+def warm_up(a, torch, step):
+    """Untimed warm-up: exactly a.warmup steps if given, else at least 5
+    steps and WARMUP_SECONDS of them (a.warmup is then set to the count)."""
+    if a.warmup is not None:
+        for _ in range(a.warmup):
+            step()
+        torch.cuda.synchronize()
+        return
+    n, t0 = 0, time.perf_counter()
+    while n < 5 or time.perf_counter() - t0 < WARMUP_SECONDS:
+        for _ in range(5):
+            step()
+        n += 5
+        torch.cuda.synchronize()
+    a.warmup = n
 
 
 def cpu_baseline(x, w, seconds):
@@ -226,9 +268,7 @@ def bench_backward(a, fp, torch, np, w, x, args, y, ws):
     torch.cuda.synchronize()
     log(f"[bench] backward: saved {saved.numel() * 4 / 2**20:.1f} MiB, "
         f"workspace {nbytes / 2**20:.1f} MiB")
-    for _ in range(a.warmup):
-        g = fp.flarepp_mixer_bwd(*args, y, dy, saved, workspace=bws)
-    torch.cuda.synchronize()
+    warm_up(a, torch, lambda: fp.flarepp_mixer_bwd(*args, y, dy, saved, workspace=bws))
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
@@ -368,9 +408,7 @@ def bench_frontend(a, fp, torch, w):
     call = lambda: fp.flarepp_frontend_fwd(d["x"], d["w_k0"], d["w_k"], d["w_v"], w.H,
                                            b_k0=d["b_k0"], b_k=d["b_k"], b_v=d["b_v"],
                                            g_k0=d["g_k0"], eps=1e-6, out=out)
-    for _ in range(a.warmup):
-        call()
-    torch.cuda.synchronize()
+    warm_up(a, torch, call)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
@@ -408,8 +446,9 @@ def bench_frontend(a, fp, torch, w):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="warm-up steps (default: as many as fill WARMUP_SECONDS)")
     ap.add_argument("--workload", default="million_token_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -464,9 +503,8 @@ def main(argv=None):
     args = (d["q0"], d["q_fixed"], d["gate"], d["k0"], d["k"], d["v"])
     if a.backward:
         return bench_backward(a, fp, torch, np, w, x, args, y, ws)
-    for _ in range(a.warmup):
-        fp.flarepp_mixer_fwd(*args, y=y, workspace=ws)
-    torch.cuda.synchronize()
+    if not a.graph:
+        warm_up(a, torch, lambda: fp.flarepp_mixer_fwd(*args, y=y, workspace=ws))
 
     # the timed region: exactly K forwards (plain calls, or replays of one
     # forward captured as a HIP graph)
@@ -481,8 +519,7 @@ def main(argv=None):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             fp.flarepp_mixer_fwd(*args, y=y, workspace=ws)
-        for _ in range(a.warmup):
-            graph.replay()
+        warm_up(a, torch, graph.replay)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
