@@ -41,7 +41,14 @@ namespace {
 using namespace flarepp;
 
 constexpr int kEncTile = 64;        // granularity of caller-chosen encoder chunks
-constexpr int kEncTargetWgs = 512;  // encoder workgroups aimed for (2 per CU)
+// encoder workgroups aimed for: one round of resident workgroups.  A 16-wave
+// workgroup (M > 256) holds a CU alone; the smaller ones fit two per CU.
+// Measured at the million-token shape: 256 workgroups of 16 waves 0.8%
+// faster than 512 (half the chunk partials to merge); at the wide-head
+// shape (4 waves) 256 was 20% slower than 512.
+inline int64_t enc_target_wgs(int64_t M, int dtype) {
+  return (dtype != FLAREPP_F32 && encode_waves((int)M) >= 16) ? 256 : 512;
+}
 struct Plan {
   int64_t B, H, N, M, D;
   int dtype;
@@ -62,10 +69,11 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   p->DV = D < 32 ? 32 : (int)D;
   const int64_t BH = B * H;
   if (chunk_tokens == 0) {
-    // automatic chunks: whole encoder tiles, about kEncTargetWgs workgroups
+    // automatic chunks: whole encoder tiles, about enc_target_wgs workgroups
     const int64_t unit = dtype == FLAREPP_F32 ? kEncTile : encode_tile_tokens();
     const int64_t tiles = (N + unit - 1) / unit;
-    int64_t c = (kEncTargetWgs + BH - 1) / BH;
+    const int64_t target = enc_target_wgs(M, dtype);
+    int64_t c = (target + BH - 1) / BH;
     if (c < 1) c = 1;
     if (c > tiles) c = tiles;
     const int64_t chunk_tiles = (tiles + c - 1) / c;

@@ -362,9 +362,9 @@ def test_noalloc_validates_before_any_device_call():
         assert L.flarepp_mixer_fwd_noalloc(1, 2, 1024, 16, 8, 1, *args, None) == HIP
     assert L.flarepp_mixer_fwd_noalloc(1, 2, 0, 16, 8, 1, *args, None) == INV
     assert L.flarepp_mixer_fwd_noalloc(1, 2, 1024, 16, 12, 1, *args, None) == UNS
-    big = (8, 16, 1 << 20, 512, 64)
+    big = (32, 16, 1 << 20, 512, 64)
     assert L.flarepp_workspace_size(*big, 1) > fp.FLAREPP_NOALLOC_SCRATCH_BYTES
-    far = [ctypes.c_void_p((i + 1) << 40) for i in range(7)]   # 17 GB tensors, disjoint
+    far = [ctypes.c_void_p((i + 1) << 40) for i in range(7)]   # 69 GB tensors, disjoint
     assert L.flarepp_mixer_fwd_noalloc(*big, 1, *far, None) == WS
     a = list(args)
     a[1] = None                                     # q_fixed
