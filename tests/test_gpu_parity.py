@@ -299,15 +299,17 @@ def test_encode_exact_recompute(fp, dtype, kind, amount):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("D", [32, 64])  # 64: rows and outputs pass the LDS staging tile
 @pytest.mark.parametrize("dtype,kind,amount", FALLBACK)
-def test_decode_exact_recompute(fp, dtype, kind, amount):
-    q, k, _ = _fallback_inputs(dtype, kind, amount, decoder=True)
+def test_decode_exact_recompute(fp, dtype, kind, amount, D):
+    # the same base-2 scores at every D: the product picks up s = 1/sqrt(D)
+    q, k, _ = _fallback_inputs(dtype, kind, amount * math.sqrt(D / 32), decoder=True, D=D)
     B, H, N, D = k.shape
     M = q.shape[1]
     rng = np.random.Generator(np.random.PCG64(5))
     z = rng.standard_normal((B, H, M, D)).astype(np.float32)
     s = 1.0 / math.sqrt(D)
-    note(f"[decode recompute] {dtype} {kind} {amount}")
+    note(f"[decode recompute] {dtype} {kind} {amount} D{D}")
     y = fp.flare_decode_fwd(torch.from_numpy(q).to(TDT[dtype]).cuda(), torch.from_numpy(z).cuda(),
                             torch.from_numpy(k).to(TDT[dtype]).cuda(), s)
     torch.cuda.synchronize()
@@ -315,7 +317,7 @@ def test_decode_exact_recompute(fp, dtype, kind, amount):
     ref = oracle.decode_ref(q.astype(np.float64), z.astype(np.float64), k.astype(np.float64), s)
     assert np.all(np.isfinite(y))
     err = rel_err(y, ref)
-    note(f"[decode recompute] {dtype} {kind} {amount} rel err {err:.3e}")
+    note(f"[decode recompute] {dtype} {kind} {amount} D{D} rel err {err:.3e}")
     assert err <= TOL[dtype]
 
 
