@@ -36,8 +36,13 @@ constexpr int kTJ = FLAREPP_ENC_TILE;  // tokens per LDS tile (chunk granularity
 // SIMD (measured -20% for the encoder at B8 H16 N16384 M128 D64 fp16).
 template <int D>
 constexpr int kTileTokens = D >= 64 ? 64 : kTJ;
-template <int D>
-constexpr int kMinWaves = D >= 64 ? 2 : 1;  // waves per SIMD the registers must allow
+// Waves per SIMD the registers must allow.  An 8-wave bf16 workgroup at
+// D <= 32 (M = 129..256) is held to 128 VGPRs, without spills, so that two
+// workgroups share a CU (it took 154, one per CU): same-box A/B at
+// B2 H8 N40000 M256 D32, synthesis 37.7 -> 33.3 us, encode unchanged; at
+// D = 16 the encode 31.7 -> 28.6 us.  fp16 would spill there and keeps 1.
+template <typename T, int D, int NW>
+constexpr int kMinWaves = D >= 64 ? 2 : (D <= 32 && NW == 8 && std::is_same<T, __bf16>::value) ? 4 : 1;
 // LDS tiles rotate over three buffers: with the score product running one
 // group ahead, a wave may still read tile t-1 while others fill tile t+1.
 constexpr int kNBUF = 3;
@@ -59,7 +64,7 @@ struct TileLayout {
 };
 
 template <typename T, int D, int NW, bool SHARED_KV>
-__global__ __launch_bounds__(64 * NW, kMinWaves<D>) void encode_split_kernel(EncodeParams a) {
+__global__ __launch_bounds__(64 * NW, (kMinWaves<T, D, NW>)) void encode_split_kernel(EncodeParams a) {
   constexpr int kTJ = kTileTokens<D>;  // tokens per LDS tile
   constexpr int kGPT = kTJ / 32;       // 32-key groups per tile
   using Tile = FlashTile<T, D, kNC>;
