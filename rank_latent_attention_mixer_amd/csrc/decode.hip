@@ -6,9 +6,9 @@
 // values z as values -- are loaded into LDS once per workgroup and stay
 // resident while the workgroup walks its token tiles (persistent over
 // tiles).  Tokens are the register side: each wave takes 32 * kNC tokens, loads
-// their k rows straight from HBM into matrix-core operands, sweeps the
-// latents 32 at a time with the shared online-softmax tile, and writes its
-// normalised y rows.  The value operand arrives with permuted rows so that
+// their k rows from HBM into matrix-core operands (directly, or at D = 64
+// through a per-wave LDS staging tile), sweeps the latents 32 at a time with
+// the shared online-softmax tile, and writes its normalised y rows.  The value operand arrives with permuted rows so that
 // each lane holds 4*NDB contiguous output columns of one token.
 #include <type_traits>
 #include <utility>

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(64 * NW, (kMinWaves<T, D, NW>)) void encode_split_k
   const int bh = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x - bh * a.nchunks;
   const int b = bh / a.H, hd = bh - b * a.H;
+  const int lat0 = (int)blockIdx.y * (NW * 32 * kNC);  // first latent of this workgroup
 
   if (a.gate != nullptr && gate_sigma(a.gate[hd]) == 0.f) return;  // closed gate: no synthesis
 
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(64 * NW, (kMinWaves<T, D, NW>)) void encode_split_k
   st.reset();
   {
     const T* qb = reinterpret_cast<const T*>(a.q) + b * a.q_b_stride + hd * a.q_h_stride;
-    const int col = wave * 32 * kNC + r;
+    const int col = lat0 + wave * 32 * kNC + r;
     const bool raw = a.qscale > 0.f;  // caller latents [.., M, D]: scale, zero rows >= M
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(64 * NW, (kMinWaves<T, D, NW>)) void encode_split_k
   auto write_partials = [&](const auto& t) {
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
-      const int col = wave * 32 * kNC + cb * 32 + r;
+      const int col = lat0 + wave * 32 * kNC + cb * 32 + r;
       const float lt = t.row_sum(cb);
       if (h == 0) {
         a.part_m[base + col] = t.reference(cb);
@@ -458,10 +459,17 @@ __global__ __launch_bounds__(512) void encode_split_f32_kernel(EncodeParams a) {
   for (int d = 0; d < D; ++d) a.part_o[base * D + d] = o[d];
 }
 
+// At D = 64 a workgroup takes at most 8 waves (256 latents): 16 waves would
+// be held to 128 VGPRs each and spill ~500 bytes per lane.  Larger M runs
+// as several latent blocks along y, each streaming the chunk's tiles.
+template <int D>
+constexpr int kMaxEncWaves = D >= 64 ? 8 : kMaxWaves;
+
 template <typename T, int D>
 hipError_t launch_mfma(const EncodeParams& p, hipStream_t s) {
-  const int nw = encode_waves(p.M);
-  const dim3 grid((unsigned)(p.B * p.H * p.nchunks));
+  const int all = encode_waves(p.M);
+  const int nw = all < kMaxEncWaves<D> ? all : kMaxEncWaves<D>;
+  const dim3 grid((unsigned)(p.B * p.H * p.nchunks), (unsigned)(all / nw));
   const bool shared_kv = (p.k == p.v);
 #define FLAREPP_ENC(NWV)                                                                     \
   case NWV:                                                                                  \
@@ -476,7 +484,14 @@ hipError_t launch_mfma(const EncodeParams& p, hipStream_t s) {
     FLAREPP_ENC(4)
     FLAREPP_ENC(8)
 #if FLAREPP_ENC_NC == 1
-    FLAREPP_ENC(16)
+    case 16:
+      if constexpr (kMaxEncWaves<D> >= 16) {
+        if (shared_kv)
+          hipLaunchKernelGGL((encode_split_kernel<T, D, 16, true>), grid, dim3(64 * 16), 0, s, p);
+        else
+          hipLaunchKernelGGL((encode_split_kernel<T, D, 16, false>), grid, dim3(64 * 16), 0, s, p);
+      }
+      break;
 #endif
     default:
       return hipErrorInvalidValue;
