@@ -462,15 +462,21 @@ __global__ __launch_bounds__(512) void encode_split_f32_kernel(EncodeParams a) {
 // At D = 64 a workgroup takes at most 8 waves (256 latents): 16 waves would
 // be held to 128 VGPRs each and spill ~500 bytes per lane.  Larger M runs
 // as several latent blocks along y, each streaming the chunk's tiles.
+// The same for the fp16 encode step (separate K and V) at D <= 32, whose
+// 16-wave form spills ~160 bytes per lane (it keeps a reference maximum):
+// same box, B1 H8 N1048576 M512 D32 fp16, encode 0.90 -> 0.74 ms.  The fp16
+// synthesis (K = V, one staged tensor) keeps 16 waves: split, it ran 9%
+// slower.
 template <int D>
 constexpr int kMaxEncWaves = D >= 64 ? 8 : kMaxWaves;
 
 template <typename T, int D>
 hipError_t launch_mfma(const EncodeParams& p, hipStream_t s) {
-  const int all = encode_waves(p.M);
-  const int nw = all < kMaxEncWaves<D> ? all : kMaxEncWaves<D>;
-  const dim3 grid((unsigned)(p.B * p.H * p.nchunks), (unsigned)(all / nw));
   const bool shared_kv = (p.k == p.v);
+  const int all = encode_waves(p.M);
+  const int cap = (std::is_same<T, _Float16>::value && !shared_kv) ? 8 : kMaxEncWaves<D>;
+  const int nw = all < cap ? all : cap;
+  const dim3 grid((unsigned)(p.B * p.H * p.nchunks), (unsigned)(all / nw));
 #define FLAREPP_ENC(NWV)                                                                     \
   case NWV:                                                                                  \
     if (shared_kv)                                                                           \
@@ -488,7 +494,7 @@ hipError_t launch_mfma(const EncodeParams& p, hipStream_t s) {
       if constexpr (kMaxEncWaves<D> >= 16) {
         if (shared_kv)
           hipLaunchKernelGGL((encode_split_kernel<T, D, 16, true>), grid, dim3(64 * 16), 0, s, p);
-        else
+        else if constexpr (!std::is_same<T, _Float16>::value)
           hipLaunchKernelGGL((encode_split_kernel<T, D, 16, false>), grid, dim3(64 * 16), 0, s, p);
       }
       break;
