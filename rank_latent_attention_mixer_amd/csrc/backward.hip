@@ -38,6 +38,10 @@
 #include "backward.hpp"
 #include "flash_tile.hpp"
 
+#ifndef FLAREPP_BWD_TOK_DEFER
+#define FLAREPP_BWD_TOK_DEFER 1
+#endif
+
 namespace flarepp {
 
 namespace {
@@ -577,9 +581,27 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
       y[db] = splat16(0.f);
       x[db] = splat16(0.f);
     }
+    // Packed operands of a group whose P.V-style products are still to be
+    // issued: at D <= 32 a group's accumulating products are deferred until
+    // the next group's score and G products are in flight, so that the
+    // matrix cores work through them while the VALU forms the next group's
+    // T (same products, same order of accumulation).  Only the FLARE pass
+    // at D <= 32 defers: at D = 64, and in the 16-wave synthesis pass held
+    // to 128 VGPRs, the held operands would not fit the registers.
+    constexpr bool kDefer = FLAREPP_BWD_TOK_DEFER && DEC && D != 64;
+    V8 pend_t[2], pend_p[2];
+    const unsigned char* pend_gb = lds_raw;
+    auto flush = [&]() {
+      V8 va[NDB][2];
+      ops.cols(pend_gb, 0, va);
+      accumulate<V8, NDB>(y, va, pend_t);
+      ops.cols(pend_gb + 2 * kTen, 0, va);
+      accumulate<V8, NDB>(x, va, pend_p);
+    };
     // one group of 32 latents; the masking of a partial last group is a
-    // compile-time variant, so full groups carry no selects
-    auto group = [&](int G, int kvalid, auto tail, auto fast_form) {
+    // compile-time variant, so full groups carry no selects.  FIRST: no
+    // earlier group is pending.
+    auto group = [&](int G, int kvalid, auto tail, auto fast_form, auto first) {
       constexpr bool FAST = decltype(fast_form)::value;
       const unsigned char* gb = lds_raw + G * kGrp;
       const float* gv = reinterpret_cast<const float*>(gb + kVec);
@@ -595,6 +617,7 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
         ops.rows(gb + kTen, 0, lop);
         g1 = product<V8, KD>(lop, b1, cg1);
       }
+      if constexpr (kDefer && !decltype(first)::value) flush();
       if constexpr (decltype(tail)::value) {
         mask_slots(s1, kvalid, h);
         if constexpr (DEC && !FAST) mask_slots(s2, kvalid, h);
@@ -616,23 +639,42 @@ __global__ __launch_bounds__((64 * tok_waves<MODE, D>())) void bwd_tok_kernel(Bw
           if constexpr (DEC) t[v] = fmaf(__builtin_amdgcn_exp2f(s2[v]), g1[v], t[v]);
         }
       }
-      V8 Tm[2], P[2];
-      pack16<T>(t, Tm);
-      pack16<T>(p, P);
-      V8 va[NDB][2];
-      ops.cols(gb, 0, va);
-      accumulate<V8, NDB>(y, va, Tm);
-      ops.cols(gb + 2 * kTen, 0, va);
-      accumulate<V8, NDB>(x, va, P);
+      if constexpr (kDefer) {
+        pack16<T>(t, pend_t);
+        pack16<T>(p, pend_p);
+        pend_gb = gb;
+      } else {
+        V8 Tm[2], P[2];
+        pack16<T>(t, Tm);
+        pack16<T>(p, P);
+        V8 va[NDB][2];
+        ops.cols(gb, 0, va);
+        accumulate<V8, NDB>(y, va, Tm);
+        ops.cols(gb + 2 * kTen, 0, va);
+        accumulate<V8, NDB>(x, va, P);
+      }
     };
     if constexpr (D == 64) {  // one code path (a second one spills at this width)
       for (int G = 0; G * 32 < a.M; ++G)
-        group(G, G < nfull ? 32 : mtail, std::true_type{}, std::false_type{});
+        group(G, G < nfull ? 32 : mtail, std::true_type{}, std::false_type{}, std::true_type{});
     } else {
       auto groups = [&](auto fast_form) {
+        if constexpr (kDefer) {
+          if (nfull > 0) {
+            group(0, 32, std::false_type{}, fast_form, std::true_type{});
 #pragma unroll 1
-        for (int G = 0; G < nfull; ++G) group(G, 32, std::false_type{}, fast_form);
-        if (mtail > 0) group(nfull, mtail, std::true_type{}, fast_form);
+            for (int G = 1; G < nfull; ++G)
+              group(G, 32, std::false_type{}, fast_form, std::false_type{});
+            if (mtail > 0) group(nfull, mtail, std::true_type{}, fast_form, std::false_type{});
+          } else {  // M < 32: the masked group alone
+            group(0, mtail, std::true_type{}, fast_form, std::true_type{});
+          }
+          flush();
+        } else {
+#pragma unroll 1
+          for (int G = 0; G < nfull; ++G) group(G, 32, std::false_type{}, fast_form, std::true_type{});
+          if (mtail > 0) group(nfull, mtail, std::true_type{}, fast_form, std::true_type{});
+        }
       };
       if constexpr (kFastForm) {
         if (fast) groups(std::true_type{});  // block-uniform
