@@ -17,8 +17,9 @@
 // register-side operand of the encoder and as the key operand of the decoder.
 //
 // Value mode (after the encode): z = merged (or a caller-given z), written
-// as the decoder's value operand: rows d permuted so that every lane ends up
-// owning contiguous output columns, latents in key-slot order.
+// as the decoder's value operand in natural [m][d] layout, rounded to the
+// operand dtype (the decoder permutes it into its matrix-core layout as it
+// fills its LDS).
 #include "flarepp_device.hpp"
 #include "kernels.hpp"
 
@@ -60,20 +61,22 @@ __device__ __forceinline__ Lse lse_merge(const Lse& a, const Lse& b) {
 // Base-2 log-sum-exp of a merged state: m + log2(l).
 __device__ __forceinline__ float lse_state_base2(float m, float l) { return m + log2f(l); }
 
-// One thread per (latent set, latent m, 4 output columns, chunk quarter):
-// each of the four lanes of a slot merges every fourth chunk, then the
-// lanes combine in a fixed butterfly and the first lane writes.
+// One thread per (latent set, latent m, 4 output columns, lane of the
+// slot): each of the L lanes of a slot (L = 1, 2, 4 or 8, fixed by the chunk
+// count) merges every L-th chunk, then the lanes combine in a fixed
+// butterfly and the first lane writes.
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
   const int set = blockIdx.x;  // sets along x: their count may pass the y limit
-  const int W4 = (a.out_kind == kOutValueT ? a.DV : a.D) / 4;
+  const int W4 = a.D / 4;
+  const int lg = a.lanes_log2, L = 1 << lg;
   const int64_t t = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
-  const int quarter = (int)(t & 3);
-  const int64_t slot = t >> 2;
+  const int sub = (int)(t & (L - 1));
+  const int64_t slot = t >> lg;
   const bool in_range = slot < (int64_t)a.Mpad * W4;  // all lanes stay for the shuffles
   const int m = in_range ? (int)(slot / W4) : 0;
   const int d0 = in_range ? 4 * (int)(slot - (int64_t)m * W4) : 0;
   const int h = set % a.H;
-  const bool live = in_range && m < a.M && d0 < a.D;  // D is a multiple of 4
+  const bool live = in_range && m < a.M;  // D is a multiple of 4
 
   float sg = 1.f;
   bool use_parts = a.nchunks > 0;
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
     if (live) {
       const int64_t base = (int64_t)set * a.nchunks * a.Mpad + m;
 #pragma unroll 4
-      for (int c = quarter; c < a.nchunks; c += 4) {
+      for (int c = sub; c < a.nchunks; c += L) {
         const int64_t i = base + (int64_t)c * a.Mpad;
         Lse x;
         x.m = a.part_m[i];
@@ -98,8 +101,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
         st = lse_merge(st, x);
       }
     }
-#pragma unroll
-    for (int x = 1; x <= 2; x <<= 1) {
+    for (int x = 1; x < L; x <<= 1) {  // L is uniform over the grid
       Lse o;
       o.m = __shfl_xor(st.m, x);
       o.l = __shfl_xor(st.l, x);
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
     lse_m = st.m;
     lse_l = st.l;
   }
-  if (!in_range || quarter != 0) return;
+  if (!in_range || sub != 0) return;
 
   float val[4] = {0.f, 0.f, 0.f, 0.f};
   if (live) {
@@ -146,29 +148,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams a) {
       }
     }
   }
-  if (a.out_kind == kOutValueT) {
-    const int col = (m & ~31) + key_slot(m & 31);
+  const int od = a.out_kind == kOutNatural32 ? (int)kF32 : a.out_dtype;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = d0 + e;
-      const int row = (d & ~31) + value_row(d & 31);  // padded columns map to zero rows
-      store_from_float(a.out, ((int64_t)set * a.DV + row) * a.Mpad + col, a.out_dtype, val[e]);
-    }
-  } else {
-    const int od = a.out_kind == kOutNatural32 ? (int)kF32 : a.out_dtype;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      store_from_float(a.out, ((int64_t)set * a.Mpad + m) * a.D + d0 + e, od, val[e]);
-  }
+  for (int e = 0; e < 4; ++e)
+    store_from_float(a.out, ((int64_t)set * a.Mpad + m) * a.D + d0 + e, od, val[e]);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
-  const int width = p.out_kind == kOutValueT ? p.DV : p.D;
-  const int64_t n = (int64_t)p.Mpad * (width / 4) * 4;  // (latent, 4 columns, chunk quarter)
-  const dim3 grid((unsigned)p.nsets, (unsigned)((n + 255) / 256));
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
+  // lanes per slot: each merges at most eight chunks, up to eight lanes
+  // (same box: with 4 chunks a lane beat four lanes of one chunk by 40%,
+  // and with 32 chunks four lanes of 8 beat eight lanes of 4 by 8%)
+  CombineParams c = p;
+  c.lanes_log2 = 0;
+  while (c.lanes_log2 < 3 && (c.nchunks + (1 << c.lanes_log2) - 1) / (1 << c.lanes_log2) > 8)
+    ++c.lanes_log2;
+  const int64_t n = ((int64_t)c.Mpad * (c.D / 4)) << c.lanes_log2;  // (latent, 4 columns, lane)
+  const dim3 grid((unsigned)c.nsets, (unsigned)((n + 255) / 256));
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, c);
   return hipGetLastError();
 }
 

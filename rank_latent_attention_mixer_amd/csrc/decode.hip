@@ -133,18 +133,27 @@ decode_kernel(DecodeParams a) {
       else w = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&qs[row * KP + 8 * e]) = w;
     }
-    const T* zg = reinterpret_cast<const T*>(a.zt) + (int64_t)bh * DV * a.Mpad;
-    const int zg8 = Mk / 8;
+    // z arrives in natural [m][d] rows; the value operand in LDS is z^T with
+    // rows d permuted (value_row) and latents in key-slot order, rows
+    // D <= d < DV zero
+    const T* zg = reinterpret_cast<const T*>(a.zt) + (int64_t)bh * a.Mpad * D;
     unsigned zb = 0u;  // max over this thread's values of |z| as ordered bits
-    for (int u = tid; u < DV * zg8; u += 64 * kNW) {
-      const int row = u / zg8, e = u - row * zg8;
-      const u32x4 v = ldg16(zg + (int64_t)row * a.Mpad + 8 * e);
-      *reinterpret_cast<u32x4*>(&zs[row * ZP + 8 * e]) = v;
+    for (int u = tid; u < Mk * G8; u += 64 * kNW) {
+      const int m = u / G8, e = u - m * G8;
+      const u32x4 v = ldg16(zg + (int64_t)m * D + 8 * e);
+      const int col = (m & ~31) + key_slot(m & 31);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float lo = (float)__builtin_bit_cast(T, (unsigned short)(v[j] & 0xFFFFu));
-        const float hi = (float)__builtin_bit_cast(T, (unsigned short)(v[j] >> 16));
-        zb = max(zb, max(__float_as_uint(fabsf(lo)), __float_as_uint(fabsf(hi))));
+      for (int j = 0; j < 8; ++j) {
+        const unsigned short bits = (unsigned short)(v[j >> 1] >> (16 * (j & 1)));
+        const int d = 8 * e + j;
+        zs[((d & ~31) + value_row(d & 31)) * ZP + col] = __builtin_bit_cast(T, bits);
+        zb = max(zb, __float_as_uint(fabsf((float)__builtin_bit_cast(T, bits))));
+      }
+    }
+    if constexpr (D < DV) {
+      for (int u = tid; u < (DV - D) * Mk; u += 64 * kNW) {
+        const int d = D + u / Mk, c = u - (u / Mk) * Mk;
+        zs[value_row(d) * ZP + c] = (T)0.f;
       }
     }
 #pragma unroll

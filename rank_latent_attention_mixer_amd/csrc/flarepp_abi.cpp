@@ -52,7 +52,7 @@ inline int64_t enc_target_wgs(int64_t M, int dtype) {
 struct Plan {
   int64_t B, H, N, M, D;
   int dtype;
-  int Mpad, DV;
+  int Mpad;
   int64_t chunk_tokens;
   int nchunks;
   int dec_wg_per_bh;
@@ -66,7 +66,6 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   if (chunk_tokens < 0 || (chunk_tokens % kEncTile) != 0) return FLAREPP_ERR_INVALID_ARGUMENT;
   p->B = B; p->H = H; p->N = N; p->M = M; p->D = D; p->dtype = dtype;
   p->Mpad = latent_pad((int)M, dtype);
-  p->DV = D < 32 ? 32 : (int)D;
   const int64_t BH = B * H;
   if (chunk_tokens == 0) {
     // automatic chunks: whole encoder tiles, about enc_target_wgs workgroups
@@ -98,9 +97,8 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t M, int64_t D, int dtype,
   p->off_pl = off; off = align_up(off + stat);
   p->off_po = off; off = align_up(off + stat * D);
   p->off_q = off;  off = align_up(off + (size_t)BH * p->Mpad * D * es);
-  p->off_z = off;
-  off = align_up(off + (dtype == FLAREPP_F32 ? (size_t)BH * p->Mpad * D * 4
-                                             : (size_t)BH * p->DV * p->Mpad * es));
+  p->off_z = off;  // value operand, natural [Mpad][D] rows (fp32 on the fp32 path)
+  off = align_up(off + (size_t)BH * p->Mpad * D * (dtype == FLAREPP_F32 ? 4 : es));
   // decoder: per (workgroup, wave) record of tiles needing the exact path
   p->off_redo = off;
   off = align_up(off + (size_t)BH * w * decode_waves((int)D) * 2 * sizeof(unsigned long long));
@@ -138,7 +136,7 @@ EncodeParams encode_params(const Plan& p, void* ws, const void* q, int64_t qb, i
 CombineParams combine_base(const Plan& p, void* ws) {
   CombineParams c;
   std::memset(&c, 0, sizeof(c));
-  c.B = (int)p.B; c.H = (int)p.H; c.M = (int)p.M; c.Mpad = p.Mpad; c.D = (int)p.D; c.DV = p.DV;
+  c.B = (int)p.B; c.H = (int)p.H; c.M = (int)p.M; c.Mpad = p.Mpad; c.D = (int)p.D;
   c.part_m = reinterpret_cast<const float*>(ws_at(ws, p.off_pm));
   c.part_l = reinterpret_cast<const float*>(ws_at(ws, p.off_pl));
   c.part_o = reinterpret_cast<const float*>(ws_at(ws, p.off_po));
@@ -156,7 +154,7 @@ hipError_t value_operand(const Plan& p, void* ws, int nchunks, const float* z_in
   c.z_out = z_out;
   c.lse_out = lse_out;
   c.out = ws_at(ws, p.off_z);
-  c.out_kind = p.dtype == FLAREPP_F32 ? kOutNatural32 : kOutValueT;
+  c.out_kind = p.dtype == FLAREPP_F32 ? kOutNatural32 : kOutNatural;
   return launch_combine(c, s);
 }
 

@@ -33,7 +33,7 @@ struct EncodeParams {
 
 // Merge of the partials plus the gated query update, or plain operand prep.
 struct CombineParams {
-  int B, H, M, Mpad, D, DV;
+  int B, H, M, Mpad, D;
   int nsets;              // latent sets written: B*H (per batch) or H (shared)
   int nchunks;            // 0: no partials
   const float* part_m;
@@ -56,12 +56,13 @@ struct CombineParams {
   float* lse_out;         // log2 of the merged row sum plus its reference (base 2)
   // operand written for the next step
   void* out;
-  int out_kind;           // kOutNatural (dtype [sets][Mpad][D]), kOutValueT (dtype
-                          // [sets][DV][Mpad], slot order), kOutNatural32 (fp32 [sets][Mpad][D])
+  int out_kind;           // kOutNatural (dtype [sets][Mpad][D]), kOutNatural32 (fp32
+                          // [sets][Mpad][D]); rows m >= M are written as zeros
   int out_dtype;
+  int lanes_log2;         // set by launch_combine: log2 of the lanes merging one slot
 };
 enum { kModeQuery = 0, kModeValue = 1 };
-enum { kOutNatural = 0, kOutValueT = 1, kOutNatural32 = 2 };
+enum { kOutNatural = 0, kOutNatural32 = 2 };
 
 // Decoder: y = softmax over latents of (k q^T) applied to z.
 struct DecodeParams {
@@ -69,8 +70,8 @@ struct DecodeParams {
                           // the caller's latents [.., M, D] unscaled
   int64_t q_b_stride, q_h_stride;
   float qscale;           // > 0: form the operand (dtype)(qscale * q) on load
-  const void* zt;         // value operand: dtype [B*H][DV][Mpad] (slot order) or
-                          // fp32 [B*H][Mpad][D] on the fp32 path
+  const void* zt;         // value operand [B*H][Mpad][D]: dtype, or fp32 on the fp32
+                          // path; rows m >= M zero
   const void* k;          // [B, H, N, D]
   void* y;                // [B, H, N, D]
   float* lse_out;         // optional [B*H, N]: per token log2(row sum) + reference
