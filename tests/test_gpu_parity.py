@@ -211,7 +211,9 @@ def test_encode_seam_and_chunk_invariance(fp, dtype):
     s = 1.0 / math.sqrt(32)
     ref = oracle.encode_ref(f64(x)["q_fixed"], f64(x)["k"], f64(x)["v"], s)
     zs = {}
-    for chunk in (0, 64, 192, 4992):
+    # 79, 27, 14, 8 and 2 chunks (plus the automatic choice): the merge
+    # takes 8, 4, 2 and 1 lanes per latent slot
+    for chunk in (0, 64, 192, 384, 640, 4992):
         z = fp.flare_encode_fwd(d["q_fixed"], d["k"], d["v"], s, chunk_tokens=chunk)
         torch.cuda.synchronize()
         zs[chunk] = z.cpu().numpy()
