@@ -337,12 +337,16 @@ __device__ __forceinline__ void wres_store(const FrontendParams& a, const WresWa
     for (int q = 0; q < kWrTok / TPI; ++q) {
       const int u = q * TPI + s.lane / CPH, c = s.lane % CPH;
       const u32x4 val = *reinterpret_cast<const u32x4*>(stg + stg_off(u, 2 * hh * D + 16 * c));
+      // non-temporal: the outputs are not read again here, and streaming
+      // them past the L2 leaves it to the x rows the other feature groups
+      // of the token range still read
       if (inside) {  // uniform base, per-lane 32-bit offset
-        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + (unsigned)(2 * (u * D + 8 * c))) = val;
+        __builtin_nontemporal_store(
+            val, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + (unsigned)(2 * (u * D + 8 * c))));
       } else if (tb + u < a.T) {
         int64_t bb = bb0, n = n0 + u;
         while (n >= a.N) { n -= a.N; ++bb; }
-        *reinterpret_cast<u32x4*>(outp + ((bb * a.H + hd) * a.N + n) * D + 8 * c) = val;
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(outp + ((bb * a.H + hd) * a.N + n) * D + 8 * c));
       }
     }
   }
