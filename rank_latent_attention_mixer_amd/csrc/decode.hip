@@ -21,6 +21,9 @@ namespace flarepp {
 namespace {
 
 // 32-token column blocks per wave and waves per workgroup (build-time knobs)
+#ifndef FLAREPP_DEC_NT_STORE
+#define FLAREPP_DEC_NT_STORE 1
+#endif
 #ifndef FLAREPP_DEC_NC
 #define FLAREPP_DEC_NC 1
 #endif
@@ -72,6 +75,17 @@ struct DecodeLds {
 // The split keeps the rare exact path's registers out of the main kernel.
 // LSE: also store each token's log2 row sum plus reference (training).
 // STAGE: token rows and outputs pass through a per-wave LDS staging tile.
+// A 16-byte store of the output y.  FLAREPP_DEC_NT_STORE: non-temporal
+// (y streams past the caches; nothing in the forward reads it again).
+template <typename T>
+__device__ __forceinline__ void y_store(T* p, u32x4 v) {
+#if FLAREPP_DEC_NT_STORE
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+#else
+  *reinterpret_cast<u32x4*>(p) = v;
+#endif
+}
+
 template <typename T, int D, bool FIXUP, bool LSE, bool STAGE>
 __global__ __launch_bounds__(64 * DecodeWaves<D>::value) void
 decode_kernel(DecodeParams a) {
@@ -276,11 +290,12 @@ auto store_tile = [&](int64_t nb, const auto& t) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) out[v] = (T)(t.o[db][cb][v] * inv);
           T* dst = STAGE ? sg + (cb * 32 + r) * SP + d0 : yg + n * D + d0;
-          if constexpr (D >= 16) {
+          if constexpr (STAGE) {
             *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
             *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(&out[8]);
-          } else {
-            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
+          } else {  // y is not read again: non-temporal stores
+            y_store(dst, *reinterpret_cast<const u32x4*>(&out[0]));
+            if constexpr (D >= 16) y_store(dst + 8, *reinterpret_cast<const u32x4*>(&out[8]));
           }
         }
       }
@@ -289,7 +304,7 @@ auto store_tile = [&](int64_t nb, const auto& t) {
         for (int i = 0; i < KD; ++i) {
           const int row = i * kRPI + srow;
           const u32x4 v = *reinterpret_cast<const u32x4*>(sg + (cb * 32 + row) * SP + scol);
-          *reinterpret_cast<u32x4*>(yg + min(nb + cb * 32 + row, a.N - 1) * D + scol) = v;
+          y_store(yg + min(nb + cb * 32 + row, a.N - 1) * D + scol, v);
         }
       }
     }
