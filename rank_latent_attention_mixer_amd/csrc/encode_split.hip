@@ -140,7 +140,9 @@ __global__ __launch_bounds__(64 * NW, (kMinWaves<T, D, NW>)) void encode_split_k
       const int row = o / L::ROWB;
       const int clog = ((o % L::ROWB) >> 4) ^ L::swz(row);
       const int eoff = min(row, lim) * D + 8 * clog;
-      global_to_lds16((ten == 0 ? kt : vt) + eoff, dst + ten * L::TILEB + li * 1024);
+      // the values are read only here; the keys are read again by the decoder
+      if (ten == 0) global_to_lds16(kt + eoff, dst + li * 1024);
+      else global_to_lds16_nt(vt + eoff, dst + ten * L::TILEB + li * 1024);
     }
   };
   // Entering tile t (buffer B = t % 3): its loads, issued one tile earlier,

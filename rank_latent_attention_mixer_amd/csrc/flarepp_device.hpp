@@ -85,6 +85,14 @@ __device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base)
                                    0);
 #endif
 }
+// The same with the non-temporal hint (data read once: it is not kept in
+// the caches at the expense of data that is read again).
+__device__ __forceinline__ void global_to_lds16_nt(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   2);
+#endif
+}
 
 // Convert 8 fp32 to a packed 8-element operand (round to nearest even).
 template <typename T>
