@@ -67,16 +67,13 @@ struct DecodeLds {
   static bool stage(int Mk) { return D >= 64 && elems(Mk, true) * 2 <= kMaxLdsBytes; }
 };
 
-// FIXUP = false: the decoder proper; a wave whose sums leave the fixed
-// reference's range records that tile (its stores still go out and are
-// overwritten later).
-// FIXUP = true: the same workgroups again, recomputing only the recorded
-// tiles by the exact two-pass method (a workgroup with none exits at once).
-// The split keeps the rare exact path's registers out of the main kernel.
-// LSE: also store each token's log2 row sum plus reference (training).
-// STAGE: token rows and outputs pass through a per-wave LDS staging tile.
-// A 16-byte store of the output y.  FLAREPP_DEC_NT_STORE: non-temporal
-// (y streams past the caches; nothing in the forward reads it again).
+// A 16-byte store of the output y from the staging tile (a wave writes a
+// contiguous KiB per instruction).  FLAREPP_DEC_NT_STORE: non-temporal, so y
+// streams past the caches (nothing in the forward reads it again) and the
+// next step's encoder does not pay for its write-back.  The unstaged path
+// (32 or 64 bytes per token row, written by two lanes) keeps plain stores:
+// non-temporal ones there left partial lines unmerged (16% more bytes
+// written at D = 32) for no gain in time.
 template <typename T>
 __device__ __forceinline__ void y_store(T* p, u32x4 v) {
 #if FLAREPP_DEC_NT_STORE
@@ -86,6 +83,14 @@ __device__ __forceinline__ void y_store(T* p, u32x4 v) {
 #endif
 }
 
+// FIXUP = false: the decoder proper; a wave whose sums leave the fixed
+// reference's range records that tile (its stores still go out and are
+// overwritten later).
+// FIXUP = true: the same workgroups again, recomputing only the recorded
+// tiles by the exact two-pass method (a workgroup with none exits at once).
+// The split keeps the rare exact path's registers out of the main kernel.
+// LSE: also store each token's log2 row sum plus reference (training).
+// STAGE: token rows and outputs pass through a per-wave LDS staging tile.
 template <typename T, int D, bool FIXUP, bool LSE, bool STAGE>
 __global__ __launch_bounds__(64 * DecodeWaves<D>::value) void
 decode_kernel(DecodeParams a) {
@@ -290,12 +295,11 @@ auto store_tile = [&](int64_t nb, const auto& t) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) out[v] = (T)(t.o[db][cb][v] * inv);
           T* dst = STAGE ? sg + (cb * 32 + r) * SP + d0 : yg + n * D + d0;
-          if constexpr (STAGE) {
+          if constexpr (D >= 16) {
             *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
             *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(&out[8]);
-          } else {  // y is not read again: non-temporal stores
-            y_store(dst, *reinterpret_cast<const u32x4*>(&out[0]));
-            if constexpr (D >= 16) y_store(dst + 8, *reinterpret_cast<const u32x4*>(&out[8]));
+          } else {
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&out[0]);
           }
         }
       }
